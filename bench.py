@@ -1,0 +1,245 @@
+"""Benchmark of the mixed-precision training hot path on one MI355X.
+
+One step = one full training step of the 12-layer GELU MLP (width 4096, batch 4096, MSE
+loss to N(0,1) targets, FP16 storage, FP32 master weights and momentum, dynamic loss
+scale starting at 2^16, SGD lr 0.01 momentum 0.9), i.e. every step of the method:
+12 forward GEMMs, the scaled loss gradient, 12 weight-gradient and 11 activation-gradient
+GEMMs, the GELU point-wise ops, the optimizer sweep (overflow check + fused update of
+201,326,592 parameters) and the scaler update. Inputs are synthetic, generated from seed 0,
+and resident in HBM before the timed region starts.
+
+Prints one JSON line. `value` is the GEMM throughput of the whole step (35 x 2 x 4096^3
+FLOP per step / step time). `roofline` is for the GEMM kernel with the largest share of
+the step, timed per launch with HIP events on the stream it runs on; the sweep's HBM
+figures are reported beside it. `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mp_step HBM GB/s + FP16/FP32-acc GEMM TFLOP/s, % of roofline, 1 MI355X"
+PEAK_F16_TFLOPS = 2500.0          # MI355X dense FP16 MFMA
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
+WIDTH, BATCH, LAYERS = 4096, 4096, 12
+SWEEP_BYTES_PER_PARAM = 20        # read g16 2 + w32 4 + v32 4, write w32 4 + v32 4 + w16 2
+CHECK_BYTES_PER_PARAM = 2
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=12, help="batch rows of the oracle's sample step")
+    return p.parse_args()
+
+
+def calibration_c() -> float:
+    with open(os.path.join(ROOT, "tests", "golden", "c4_calibration.json")) as f:
+        return float(json.load(f)["c"])
+
+
+class Model:
+    """Device state of the C4 workload and one training step through libmp."""
+
+    def __init__(self, mp, torch, w, c):
+        self.mp, self.torch, self.c = mp, torch, c
+        dev = "cuda"
+        f16 = torch.float16
+        self.W = [torch.from_numpy(m).to(dev) for m in w.masters]
+        self.V = [torch.zeros_like(m) for m in self.W]
+        self.W16 = [mp.round_f32_to_f16(m) for m in self.W]
+        self.G = [torch.empty((WIDTH, WIDTH), dtype=f16, device=dev) for _ in range(LAYERS)]
+        import numpy as np
+        self.X = torch.from_numpy(w.X16.view(np.int16)).to(dev).view(f16)
+        self.T = torch.from_numpy(w.T16.view(np.int16)).to(dev).view(f16)
+        self.Z = [torch.empty((BATCH, WIDTH), dtype=f16, device=dev) for _ in range(LAYERS)]
+        self.H = [torch.empty((BATCH, WIDTH), dtype=f16, device=dev) for _ in range(LAYERS - 1)]
+        self.dA = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)
+        self.dB = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.scaler = mp.Scaler(w.scale, w.dynamic, w.growth_interval)
+        self.plist = mp.ParamList(self.W, self.V, self.G, self.W16)
+        self.hp = (w.lr, w.momentum, w.weight_decay)
+        self.events = None
+
+    def _t(self, kind, fn, *a, **k):
+        if self.events is None:
+            return fn(*a, **k)
+        E = self.torch.cuda.Event
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        e0.record()
+        r = fn(*a, **k)
+        e1.record()
+        self.events.setdefault(kind, []).append((e0, e1))
+        return r
+
+    def step(self):
+        mp, t = self.mp, self._t
+        inp = self.X
+        for l in range(LAYERS):
+            t("fwd", mp.linear_fwd, inp, self.W16[l], Y=self.Z[l])
+            if l < LAYERS - 1:
+                t("gelu_fwd", mp.act_fwd, mp.GELU, self.Z[l], self.H[l])
+                inp = self.H[l]
+        t("loss", mp.loss_mse, self.Z[-1], self.T, self.c, self.scaler, self.loss, self.dA)
+        dZ, dH = self.dA, self.dB
+        for l in range(LAYERS - 1, -1, -1):
+            if l < LAYERS - 1:
+                t("gelu_bwd", mp.act_bwd, mp.GELU, self.Z[l], dH, dZ)
+            prev = self.X if l == 0 else self.H[l - 1]
+            t("wgrad", mp.linear_wgrad, dZ, prev, dW=self.G[l])
+            if l > 0:
+                t("dgrad", mp.linear_dgrad, dZ, self.W16[l], dX=dH)
+        lr, mu, wd = self.hp
+        t("sweep", mp.step, self.plist, self.scaler, lr, mu, wd)
+        t("scaler", self.scaler.update)
+
+    def kernel_ms(self):
+        out = {}
+        for k, evs in self.events.items():
+            d = [a.elapsed_time(b) for a, b in evs]
+            out[k] = {"launches": len(d), "avg_ms": sum(d) / len(d), "total_ms": sum(d)}
+        return out
+
+
+def cpu_baseline(w, c, rows):
+    """The oracle on a bounded sample of the same step: all 35 GEMMs of the step on `rows` of the
+    4096 batch rows (rows are independent in forward and dgrad; wgrad reduces over those rows),
+    the point-wise ops and the loss on those rows, and the full optimizer sweep."""
+    import numpy as np
+
+    import oracle
+    W16 = [oracle.f32_to_f16(m) for m in w.masters]
+    X, T = w.X16[:rows].copy(), w.T16[:rows].copy()
+    t0 = time.perf_counter()
+    Z, H = [], [X]
+    for l in range(LAYERS):
+        Z.append(oracle.linear_fwd(H[-1], W16[l], out_f16=True))
+        if l < LAYERS - 1:
+            H.append(oracle.gelu_fwd(Z[-1]))
+    _, dZ = oracle.mse(Z[-1], T, c * rows / BATCH, w.scale)
+    grads = [None] * LAYERS
+    for l in range(LAYERS - 1, -1, -1):
+        grads[l] = oracle.linear_wgrad(dZ, H[l], out_f16=True)
+        if l > 0:
+            dH = oracle.linear_dgrad(dZ, W16[l], out_f16=True)
+            dZ = oracle.gelu_bwd(Z[l - 1], dH)
+    t_gemm = time.perf_counter() - t0
+    masters = [m.reshape(-1).copy() for m in w.masters]
+    moms = [np.zeros_like(m) for m in masters]
+    w16 = [x.reshape(-1).copy() for x in W16]
+    t1 = time.perf_counter()
+    oracle.step(masters, moms, [g.reshape(-1) for g in grads], w16, w.lr, w.momentum,
+                w.weight_decay, 1.0 / w.scale)
+    t_sweep = time.perf_counter() - t1
+    gemm_flops = 2.0 * rows * WIDTH * WIDTH * (3 * LAYERS - 1)
+    nparam = LAYERS * WIDTH * WIDTH
+    return {
+        "value": gemm_flops / t_gemm / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"C4 step on {rows} of {BATCH} batch rows: 35 GEMMs (2*{rows}*4096*4096 FLOP "
+                  f"each), GELU and loss on those rows ({t_gemm:.2f} s); full optimizer sweep over "
+                  f"{nparam} parameters ({t_sweep:.2f} s)",
+        "sweep_GBps": SWEEP_BYTES_PER_PARAM * nparam / t_sweep / 1e9,
+        "seconds": round(t_gemm + t_sweep, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import mixed_precision_neural_amd as mp
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    c = calibration_c()
+    w = workloads.c4()
+    model = Model(mp, torch, w, c)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        model.step()
+    torch.cuda.synchronize()
+
+    model.events = {}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        model.step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    kern = model.kernel_ms()
+    st = model.scaler.read()
+
+    gemm_flop = 2.0 * WIDTH * WIDTH * BATCH
+    step_flop = gemm_flop * (3 * LAYERS - 1)
+    value = step_flop / (ms * 1e-3) / 1e12
+    gemm = {}
+    for k in ("fwd", "dgrad", "wgrad"):
+        tf = gemm_flop / (kern[k]["avg_ms"] * 1e-3) / 1e12
+        gemm[k] = {"avg_us": round(kern[k]["avg_ms"] * 1e3, 2), "TFLOPs": round(tf, 1),
+                   "frac": round(tf / PEAK_F16_TFLOPS, 4), "launches": kern[k]["launches"]}
+    dom = max(("fwd", "dgrad", "wgrad"), key=lambda k: kern[k]["total_ms"])
+    nparam = LAYERS * WIDTH * WIDTH
+    sweep_ms = kern["sweep"]["avg_ms"]
+    sweep_gbps = SWEEP_BYTES_PER_PARAM * nparam / (sweep_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16/f32",
+        "data": "synthetic",
+        "config": {"workload": "C4: 12-layer GELU MLP, width 4096, batch 4096, MSE to N(0,1) targets, "
+                               "FP16 storage, FP32 master + momentum, dynamic loss scale 2^16, "
+                               "SGD lr 0.01 momentum 0.9",
+                   "global_batch": BATCH, "params": nparam, "gemms_per_step": 3 * LAYERS - 1,
+                   "loss_multiplier_c": c},
+        "roofline": {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": gemm[dom]["TFLOPs"],
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": gemm[dom]["frac"],
+                     "traffic": None},
+        "gemm": gemm,
+        "mp_step": {"bound": "hbm", "avg_us": round(sweep_ms * 1e3, 2),
+                    "achieved_GBps": round(sweep_gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "frac": round(sweep_gbps / PEAK_HBM_GBPS, 4),
+                    "algorithmic_bytes": SWEEP_BYTES_PER_PARAM * nparam,
+                    "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam},
+        "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")},
+        "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, c, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+/*
+ * libmp — the mixed-precision training hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Mixed Precision Training", long-form analysis page,
+ * paper-graph-ui.vercel.app, §3.2 and §3.4 "The Integrated Training
+ * Procedure", Steps 1-7):
+ *   binary16 weights, activations and gradients; dot products with binary16
+ *   inputs and FP32 accumulation; an FP32 master copy of every weight; the
+ *   loss multiplied by a scale S before back-propagation; weight gradients
+ *   divided by S, checked for inf/NaN, the whole update skipped on overflow,
+ *   otherwise SGD with momentum (and coupled weight decay) on the FP32
+ *   masters, which are rounded back to binary16; S adjusted afterwards.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers unless stated otherwise. binary16 data is passed as
+ *     uint16_t bit patterns (IEEE 754 binary16), FP32 as float.
+ *   - Matrices are row-major with an explicit leading dimension (elements
+ *     between consecutive rows). Weights follow the out x in convention:
+ *     W[N, K] maps K inputs to N outputs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is stream-ordered and asynchronous: no entry point
+ *     synchronises the host or reads device results on the host.
+ *   - Argument errors are detected on the host before anything is launched
+ *     and returned as a status; a launch failure returns MP_ERR_HIP and
+ *     mp_last_hip_error() names it. Faults inside kernels surface at the
+ *     caller's next synchronisation. No C++ exception crosses this ABI.
+ *   - A zero M, N, numel or list length is a successful no-op; K = 0 (an
+ *     empty reduction) writes zeros.
+ *   - The caller owns every data buffer and every mp_scaler. The library
+ *     owns only mp_param_list handles (created and destroyed here).
+ *   - Outputs must not alias inputs, except that master weights and momentum
+ *     are updated in place by design.
+ *   - Calls on different streams are safe when their buffers are disjoint;
+ *     one mp_scaler belongs to one stream at a time.
+ */
+#ifndef MP_H
+#define MP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MP_OK = 0,
+    MP_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad leading dim, bad scale */
+    MP_ERR_MISALIGNED = 2,         /* reserved: every entry point has an unaligned path      */
+    MP_ERR_UNSUPPORTED = 3,        /* a flag or dtype this build does not implement          */
+    MP_ERR_HIP = 4,                /* a HIP runtime call failed; see mp_last_hip_error()     */
+    MP_ERR_OUT_OF_MEMORY = 5       /* allocation of a library-owned handle failed            */
+} mp_status;
+
+typedef enum { MP_F16 = 0, MP_F32 = 1 } mp_dtype;
+
+/* Loss-scaler state, resident in device memory (caller-allocated, 32 bytes,
+ * 4-byte aligned). `scale` is always a power of two in [1, 2^64];
+ * `inv_scale` is its exact reciprocal. `found_inf` is the overflow flag of
+ * the step in progress: it must be 0 when a step starts (mp_scaler_init and
+ * mp_scaler_update leave it 0) and only ever goes 0 -> 1 during a step. */
+typedef struct mp_scaler {
+    float    scale;
+    float    inv_scale;
+    int32_t  count;            /* consecutive clean steps since the last change */
+    int32_t  growth_interval;  /* clean steps after which S doubles (dynamic)   */
+    uint32_t found_inf;
+    uint32_t dynamic;          /* 0: constant S (method 1); 1: dynamic (method 3) */
+    uint32_t skipped_steps;    /* steps skipped because of overflow             */
+    uint32_t reserved;
+} mp_scaler;
+
+/* SGD-with-momentum hyper-parameters, passed by value. */
+typedef struct mp_sgd {
+    float lr;
+    float momentum;
+    float weight_decay;
+} mp_sgd;
+
+/* One parameter tensor of the optimizer sweep (host-side description). */
+typedef struct mp_param {
+    float*          master;    /* FP32 master weights [numel], updated in place */
+    float*          momentum;  /* FP32 velocity [numel], updated in place       */
+    const uint16_t* grad;      /* binary16 loss-scaled gradient [numel], read   */
+    uint16_t*       weight16;  /* binary16 working copy [numel], rewritten      */
+    int64_t         numel;
+} mp_param;
+
+typedef struct mp_param_list mp_param_list;
+
+typedef void* mp_stream;
+
+/* ------------------------------------------------------------------------
+ * Dot-product layers: binary16 inputs, exact products, FP32 accumulation,
+ * output rounded to nearest-even binary16 (overflow gives +-inf, never a
+ * saturated 65504) or written as FP32. Source: the analysis page, §3.4
+ * "FP16 Arithmetic with FP32 Accumulation" and "The Integrated Training
+ * Procedure", Steps 2 and 4. Summation order inside a dot product is the
+ * kernel's (tiled); results agree with an ascending-order FP32 sum within
+ * the rounding error of FP32 accumulation.
+ * ------------------------------------------------------------------------ */
+
+/* Forward: Y[M, N] = X[M, K] . W[N, K]^T.
+ * X: ldx >= K; W: ldw >= K; Y: ldy >= N, element type y_dtype.
+ * Errors: MP_ERR_INVALID_ARGUMENT for negative sizes, a leading dimension
+ * smaller than its row, or a null pointer with a non-empty matrix. */
+mp_status mp_linear_fwd(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                        void* Y, int64_t ldy, mp_dtype y_dtype,
+                        int64_t M, int64_t N, int64_t K, mp_stream stream);
+
+/* Activation gradient: dX[M, K] = dY[M, N] . W[N, K]. The result stays
+ * multiplied by the loss scale (Step 4: activation gradients are never
+ * unscaled). dY: lddy >= N; W: ldw >= K; dX: lddx >= K. */
+mp_status mp_linear_dgrad(const uint16_t* dY, int64_t lddy, const uint16_t* W, int64_t ldw,
+                          void* dX, int64_t lddx, mp_dtype dx_dtype,
+                          int64_t M, int64_t N, int64_t K, mp_stream stream);
+
+/* Weight gradient: dW[N, K] = dY[M, N]^T . X[M, K] (overwritten, not
+ * accumulated). dY: lddy >= N; X: ldx >= K; dW: lddw >= K.
+ * found_inf (nullable, device uint32): when given, the kernel ORs 1 into it
+ * if any stored binary16 output is +-inf or NaN, so that mp_step can be
+ * called with MP_GRADS_PRECHECKED (Step 6 fused into the producer). With an
+ * FP32 output found_inf must be NULL (MP_ERR_INVALID_ARGUMENT otherwise). */
+mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uint16_t* X, int64_t ldx,
+                          void* dW, int64_t lddw, mp_dtype dw_dtype,
+                          int64_t M, int64_t N, int64_t K, uint32_t* found_inf,
+                          mp_stream stream);
+
+/* ------------------------------------------------------------------------
+ * The optimizer sweep over a ragged list of parameter tensors.
+ * Source: the analysis page, §3.4 "The Integrated Training Procedure",
+ * Steps 5-7 and the weight-decay paragraph.
+ * ------------------------------------------------------------------------ */
+
+/* Copies the n descriptors (host array, read during the call only) into a
+ * library-owned device table and chunk map. Tensors may have any length; a
+ * tensor whose four base addresses are all 16-byte aligned takes the
+ * vectorised path, any other tensor a scalar path with the same results.
+ * Every non-empty tensor needs four non-null pointers; empty tensors are
+ * allowed and ignored. The list remembers the pointers, not the data: the
+ * buffers must stay allocated while the list is used.
+ * Errors: MP_ERR_INVALID_ARGUMENT (n < 0, out == NULL, null pointer with
+ * numel > 0, numel < 0), MP_ERR_OUT_OF_MEMORY, MP_ERR_HIP. */
+mp_status mp_param_list_create(const mp_param* host_params, int32_t n,
+                               mp_param_list** out, mp_stream stream);
+
+/* Frees the handle after the work queued on `stream` at creation has
+ * finished (it synchronises that stream). NULL is accepted. */
+mp_status mp_param_list_destroy(mp_param_list* list);
+
+/* Total number of elements in the list (host value). */
+int64_t mp_param_list_numel(const mp_param_list* list);
+
+enum {
+    MP_STEP_DEFAULT = 0,
+    /* Skip the check pass: the gradients were produced by mp_linear_wgrad
+     * with found_inf = &scaler->found_inf, which already holds the flag. */
+    MP_GRADS_PRECHECKED = 1u << 0
+};
+
+/* One optimizer step. For every element of every tensor, in FP32 with one
+ * rounding per operation and no fused multiply-add:
+ *     g  = f32(grad16) * inv_scale         (Step 5: unscale, exact)
+ *     g  = g + weight_decay * master       (coupled L2 on the FP32 master)
+ *     v  = momentum * v + g                (Step 7)
+ *     w  = w - lr * v                      (Step 7)
+ *     weight16 = round-to-nearest-even binary16 of w   (Step 1)
+ * but only if no gradient element of any tensor is +-inf or NaN (Step 6).
+ * Otherwise nothing is written (masters, momentum and binary16 copies keep
+ * their bits) and scaler->found_inf is 1 afterwards. inv_scale and the flag
+ * are read from `scaler` on the device. The gradients are never written.
+ * Implementation: a read-only check pass over all gradients (skipped with
+ * MP_GRADS_PRECHECKED) followed by one fused update pass that exits at once
+ * when the flag is set.
+ * Errors: MP_ERR_INVALID_ARGUMENT (list or scaler NULL), MP_ERR_UNSUPPORTED
+ * (unknown flag bits), MP_ERR_HIP. */
+mp_status mp_step(const mp_param_list* list, mp_sgd hyper, mp_scaler* scaler,
+                  uint32_t flags, mp_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Loss scaler. Source: the analysis page, §3.4 "Choosing the Loss Scaling
+ * Factor": method 1 (constant S, an overflowing step is skipped) and
+ * method 3 (dynamic: on overflow skip and halve S; after growth_interval
+ * consecutive clean steps double S).
+ * ------------------------------------------------------------------------ */
+
+/* Writes a fresh state: scale = init_scale, count = 0, found_inf = 0,
+ * skipped_steps = 0. init_scale must be a power of two in [1, 2^64];
+ * growth_interval >= 1 when dynamic. */
+mp_status mp_scaler_init(mp_scaler* scaler, float init_scale, int32_t dynamic,
+                         int32_t growth_interval, mp_stream stream);
+
+/* Consumes found_inf of the finished step: on overflow skipped_steps += 1
+ * and, when dynamic, scale halves (not below 1) and count = 0; on a clean
+ * dynamic step count += 1 and, when it reaches growth_interval, scale
+ * doubles (not above 2^64) and count = 0. Then inv_scale = 1/scale and
+ * found_inf = 0. One single-lane kernel; no host round trip. */
+mp_status mp_scaler_update(mp_scaler* scaler, mp_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Auxiliary steps that a full training step needs around the hot path.
+ * Point-wise ops run in FP32 on binary16 data; the losses reduce in FP32
+ * (the analysis page, §3.4: point-wise ops in either precision, large
+ * reductions in FP32). Loss gradients are multiplied by the device-resident
+ * scale S in FP32 and rounded once to binary16 (Step 3).
+ * ------------------------------------------------------------------------ */
+
+/* w16[i] = round-to-nearest-even binary16 of w32[i] (Step 1 at init). */
+mp_status mp_round_f32_to_f16(const float* w32, uint16_t* w16, int64_t n, mp_stream stream);
+
+typedef enum { MP_ACT_RELU = 0, MP_ACT_GELU = 1 } mp_act;
+
+/* y = act(x), elementwise over n binary16 values. GELU is x * Phi(x) with
+ * the exact error function. */
+mp_status mp_act_fwd(mp_act kind, const uint16_t* x, uint16_t* y, int64_t n, mp_stream stream);
+
+/* dx = dy * act'(x), elementwise; x is the saved pre-activation. */
+mp_status mp_act_bwd(mp_act kind, const uint16_t* x, const uint16_t* dy, uint16_t* dx,
+                     int64_t n, mp_stream stream);
+
+/* Mean softmax cross-entropy over B rows of C logits (binary16, row-major,
+ * contiguous) with int32 labels in [0, C). Writes the FP32 loss to *loss
+ * (device) and dlogits = RNE16(S * (softmax - onehot) / B) with S read from
+ * `scaler`. Labels live on the device, so their range is the caller's
+ * responsibility: a label outside [0, C) contributes no one-hot term. */
+mp_status mp_loss_softmax_ce(const uint16_t* logits, const int32_t* labels, int64_t B,
+                             int64_t C, const mp_scaler* scaler, float* loss,
+                             uint16_t* dlogits, mp_stream stream);
+
+/* Mean squared error times c over the M x N elements (binary16, contiguous):
+ * *loss = c * mean((y - t)^2) (FP32, device), dy = RNE16(S * c * 2 (y - t) / (M N)).
+ * The sum is reduced in a fixed order (per-block partials in a library-owned
+ * device array, then one block), so the loss is deterministic; concurrent
+ * loss calls on one GPU share that array and must not overlap. */
+mp_status mp_loss_mse(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N, float c,
+                      const mp_scaler* scaler, float* loss, uint16_t* dy, mp_stream stream);
+
+/* ------------------------------------------------------------------------ */
+const char* mp_status_string(mp_status status);
+/* The last HIP error seen by this library on the calling thread ("" if none). */
+const char* mp_last_hip_error(void);
+/* Library version string. */
+const char* mp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,81 @@
+"""GPU parity of the point-wise activations and the losses against the oracle.
+
+Source: "Mixed Precision Training", long-form analysis page, §3.4 "FP16 Arithmetic
+with FP32 Accumulation" (point-wise ops, FP32 reductions) and "The Integrated
+Training Procedure", Step 3 (loss scaling). ReLU is exact; GELU and the loss
+gradients are FP32 on the GPU against a double-precision oracle and must agree
+within one binary16 ulp (2^-10 relative, 2^-24 absolute near zero).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_neural_amd as mp
+import oracle
+from gpu_util import dev_f16, f16_values, host_bits16, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def within_ulp(got_bits, ref_bits, ulps=1):
+    g, r = f16_values(got_bits), f16_values(ref_bits)
+    tol = np.maximum(np.abs(r) * 2.0 ** -10 * ulps, 2.0 ** -24 * ulps)
+    both_nan = np.isnan(g) & np.isnan(r)
+    same_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
+    return bool(np.all(both_nan | same_inf | (np.abs(g - r) <= tol)))
+
+
+def all_finite_f16():
+    h = np.arange(1 << 16, dtype=np.uint16)
+    return h[(h & 0x7C00) != 0x7C00]
+
+
+@pytest.mark.parametrize("n", [1, 9, 63488, 100001])
+def test_relu_exact(n):
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(n))
+    x = all_finite_f16() if n == 63488 else rng.integers(0, 1 << 16, n).astype(np.uint16)
+    dy = rng.integers(0, 1 << 16, x.size).astype(np.uint16)
+    y = host_bits16(mp.act_fwd(mp.RELU, dev_f16(x)))
+    dx = host_bits16(mp.act_bwd(mp.RELU, dev_f16(x), dev_f16(dy)))
+    assert np.array_equal(y, oracle.relu_fwd(x))
+    assert np.array_equal(dx, oracle.relu_bwd(x, dy))
+
+
+def test_gelu_all_finite_inputs():
+    require_gpu()
+    x = all_finite_f16()
+    y = host_bits16(mp.act_fwd(mp.GELU, dev_f16(x)))
+    assert within_ulp(y, oracle.gelu_fwd(x))
+    rng = np.random.Generator(np.random.PCG64(1))
+    dy = rng.standard_normal(x.size).astype(np.float16).view(np.uint16)
+    dx = host_bits16(mp.act_bwd(mp.GELU, dev_f16(x), dev_f16(dy)))
+    assert within_ulp(dx, oracle.gelu_bwd(x, dy), ulps=2)
+
+
+@pytest.mark.parametrize("B,C,S", [(64, 10, 1024.0), (7, 1000, 8.0), (300, 3, 2.0 ** 15)])
+def test_softmax_cross_entropy(B, C, S):
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(B * C))
+    z = (rng.standard_normal((B, C)) * 4).astype(np.float16).view(np.uint16)
+    y = rng.integers(0, C, B).astype(np.int32)
+    sc = mp.Scaler(S, False)
+    loss, d = mp.loss_softmax_ce(dev_f16(z), torch.from_numpy(y).cuda(), sc)
+    ref_loss, ref_d = oracle.softmax_ce(z, y, S)
+    assert math.isclose(float(loss.item()), ref_loss, rel_tol=1e-5)
+    assert within_ulp(host_bits16(d), ref_d, ulps=2)
+
+
+@pytest.mark.parametrize("M,N,c,S", [(64, 50, 1.0, 1.0), (333, 257, 3.5, 2.0 ** 16), (1024, 1024, 1e4, 2.0 ** 10)])
+def test_mse(M, N, c, S):
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(M))
+    yb = rng.standard_normal((M, N)).astype(np.float16).view(np.uint16)
+    tb = rng.standard_normal((M, N)).astype(np.float16).view(np.uint16)
+    sc = mp.Scaler(S, True)
+    loss, d = mp.loss_mse(dev_f16(yb), dev_f16(tb), c, sc)
+    ref_loss, ref_d = oracle.mse(yb, tb, c, S)
+    assert math.isclose(float(loss.item()), ref_loss, rel_tol=1e-5)
+    assert within_ulp(host_bits16(d), ref_d, ulps=2)

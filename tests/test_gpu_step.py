@@ -1,0 +1,278 @@
+"""GPU parity of the optimizer sweep and the loss scaler against the oracle (bit-exact).
+
+Source: "Mixed Precision Training", long-form analysis page, §3.4 "The Integrated
+Training Procedure" (Steps 1, 5-7, weight decay) and "Choosing the Loss Scaling
+Factor" (methods 1 and 3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_neural_amd as mp
+import oracle
+import workloads
+from gpu_util import (dev_f16, dev_f32, host_bits16, host_f32, require_gpu, same_f16_bits,
+                      same_f32_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+class Run:
+    """The same tensors on the GPU and on the host, stepped by libmp and by the oracle."""
+
+    def __init__(self, ws, vs, gs):
+        self.h_w = [np.array(w, np.float32) for w in ws]
+        self.h_v = [np.array(v, np.float32) for v in vs]
+        self.h_g = [np.array(g, np.uint16) for g in gs]
+        self.h_16 = [oracle.f32_to_f16(w) for w in self.h_w]
+        self.d_w = [dev_f32(w) for w in self.h_w]
+        self.d_v = [dev_f32(v) for v in self.h_v]
+        self.d_g = [dev_f16(g) for g in self.h_g]
+        self.d_16 = [mp.round_f32_to_f16(w) for w in self.d_w]
+
+    def plist(self):
+        return mp.ParamList(self.d_w, self.d_v, self.d_g, self.d_16)
+
+    def set_grads(self, gs):
+        for i, g in enumerate(gs):
+            self.h_g[i][:] = g
+            self.d_g[i].copy_(dev_f16(g))
+
+    def oracle_step(self, lr, mu, wd, inv_scale):
+        return oracle.step(self.h_w, self.h_v, self.h_g, self.h_16, lr, mu, wd, inv_scale)
+
+    def assert_equal(self, what=""):
+        torch.cuda.synchronize()
+        for i in range(len(self.h_w)):
+            assert same_f32_bits(host_f32(self.d_w[i]), self.h_w[i]), f"master {i} {what}"
+            assert same_f32_bits(host_f32(self.d_v[i]), self.h_v[i]), f"momentum {i} {what}"
+            assert same_f16_bits(host_bits16(self.d_16[i]), self.h_16[i]), f"weight16 {i} {what}"
+
+
+def scaler_pair(scale, dynamic, interval=2000):
+    return mp.Scaler(scale, dynamic, interval), oracle.scaler_init(scale, dynamic, interval)
+
+
+def assert_scaler(d: mp.Scaler, o):
+    got = d.read()
+    for k in ("scale", "inv_scale", "count", "growth_interval", "found_inf", "dynamic", "skipped_steps"):
+        assert got[k] == getattr(o, k), (k, got[k], getattr(o, k))
+
+
+def test_round_init_matches_oracle():
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(0))
+    for n in (1, 7, 8, 1000, 65539):
+        w = (rng.standard_normal(n) * rng.choice([1e-8, 1e-3, 1.0, 1e4, 7e4], n)).astype(np.float32)
+        got = host_bits16(mp.round_f32_to_f16(dev_f32(w)))
+        assert same_f16_bits(got, oracle.f32_to_f16(w)), n
+
+
+@pytest.mark.parametrize("lr,mu,wd", [(0.01, 0.9, 0.0), (1e-3, 0.9, 1e-4), (2.0 ** -11, 0.0, 0.5)])
+@pytest.mark.parametrize("scale_log2", [0, 10, 15, 24, 64])
+def test_every_finite_f16_gradient_pattern(lr, mu, wd, scale_log2):
+    """Pin P11: every finite binary16 gradient pattern, with masters and momenta drawn from edge
+    values (signed zeros, FP32 subnormals, binary16 rounding ties and the overflow boundary)."""
+    require_gpu()
+    h = np.arange(1 << 16, dtype=np.uint16)
+    g = h[(h & 0x7C00) != 0x7C00]
+    edges = np.array([0.0, -0.0, 1.0, -1.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 1.0 - 2 ** -12,
+                      2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25, 1e-40, -1e-40, 65504.0,
+                      65519.0, 65520.0, -65536.0, 1e30, 0.1, -0.3, 123.456], np.float32)
+    n = g.size
+    w = edges[np.arange(n) % edges.size]
+    v = edges[(np.arange(n) // edges.size) % edges.size]
+    r = Run([w], [v], [g])
+    S = mp.Scaler(2.0 ** scale_log2, True)
+    pl = r.plist()
+    mp.step(pl, S, lr, mu, wd)
+    flag = r.oracle_step(lr, mu, wd, 2.0 ** -scale_log2)
+    assert flag == 0
+    r.assert_equal()
+    assert S.read()["found_inf"] == 0
+    pl.close()
+
+
+@pytest.mark.parametrize("bad", [0x7C00, 0xFC00, 0x7E00, 0xFE01, 0x7C01])
+@pytest.mark.parametrize("where", ["first", "middle", "last"])
+@pytest.mark.parametrize("tensor", [0, 2])
+def test_overflow_anywhere_skips_everything(bad, where, tensor):
+    """Pin P6: one non-finite gradient element anywhere in the ragged list: no bit of any master,
+    momentum or binary16 copy changes; dynamic S halves, count resets, skipped_steps += 1."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(5))
+    sizes = [8193, 7, 20000]
+    ws = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    vs = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    gs = [(rng.standard_normal(n) * 100).astype(np.float16).view(np.uint16) for n in sizes]
+    idx = {"first": 0, "middle": sizes[tensor] // 2, "last": sizes[tensor] - 1}[where]
+    gs[tensor][idx] = bad
+    r = Run(ws, vs, gs)
+    before = [host_f32(t).copy() for t in r.d_w + r.d_v] + [host_bits16(t).copy() for t in r.d_16]
+    dS, oS = scaler_pair(2.0 ** 15, True)
+    pl = r.plist()
+    mp.step(pl, dS, 0.01, 0.9, 1e-4)
+    assert dS.read()["found_inf"] == 1
+    flag = r.oracle_step(0.01, 0.9, 1e-4, oS.inv_scale)
+    assert flag == 1
+    after = [host_f32(t) for t in r.d_w + r.d_v] + [host_bits16(t) for t in r.d_16]
+    for a, b in zip(after, before):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    dS.update(); oracle.scaler_update(oS, flag)
+    assert_scaler(dS, oS)
+    assert dS.read()["scale"] == 2.0 ** 14
+    pl.close()
+
+
+def test_static_scaler_overflow_keeps_scale():
+    require_gpu()
+    r = Run([np.ones(100, np.float32)], [np.zeros(100, np.float32)], [np.full(100, 0x7C00, np.uint16)])
+    dS, oS = scaler_pair(1024.0, False)
+    pl = r.plist()
+    mp.step(pl, dS, 0.01, 0.9, 0.0)
+    flag = r.oracle_step(0.01, 0.9, 0.0, oS.inv_scale)
+    dS.update(); oracle.scaler_update(oS, flag)
+    assert_scaler(dS, oS)
+    assert dS.read()["scale"] == 1024.0 and dS.read()["skipped_steps"] == 1
+    pl.close()
+
+
+def test_scaler_growth_and_clamps():
+    require_gpu()
+    for init, dyn, interval, flags in [(8.0, True, 3, [0, 0, 0, 0, 0, 1, 0, 0, 0]),
+                                       (1.0, True, 1, [1, 1, 0]),
+                                       (2.0 ** 63, True, 1, [0, 0, 0]),
+                                       (1024.0, False, 2, [0, 1, 0, 0])]:
+        dS, oS = scaler_pair(init, dyn, interval)
+        for f in flags:
+            if f:
+                dS.buf[4] = 1
+            dS.update()
+            oracle.scaler_update(oS, f)
+            assert_scaler(dS, oS)
+
+
+@pytest.mark.parametrize("sizes", [[1], [7, 8, 9], [8191, 8192, 8193], [1, 100000, 3, 65536 * 3 + 5]])
+def test_ragged_lists_multi_step(sizes):
+    """Several clean steps over ragged lists with tails shorter than a vector and a chunk."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(len(sizes)))
+    ws = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    vs = [np.zeros(n, np.float32) for n in sizes]
+    g_true = [(rng.standard_normal(n) * 2.0 ** -12).astype(np.float32) for n in sizes]
+    gs = [workloads.grads_at_scale(g, 2.0 ** 12) for g in g_true]
+    r = Run(ws, vs, gs)
+    dS, oS = scaler_pair(2.0 ** 12, True, 2)
+    pl = r.plist()
+    for t in range(5):
+        mp.step(pl, dS, 1e-3, 0.9, 1e-4)
+        flag = r.oracle_step(1e-3, 0.9, 1e-4, oS.inv_scale)
+        dS.update(); oracle.scaler_update(oS, flag)
+        r.assert_equal(f"step {t}")
+        assert_scaler(dS, oS)
+        r.set_grads([workloads.grads_at_scale(g, oS.scale) for g in g_true])
+    pl.close()
+
+
+def test_unaligned_tensors_take_the_scalar_path():
+    """Views that start one element into an allocation break 16-byte alignment."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(9))
+    n = 50001
+    base_w = dev_f32(rng.standard_normal(n + 1).astype(np.float32))
+    base_v = dev_f32(rng.standard_normal(n + 1).astype(np.float32))
+    g = (rng.standard_normal(n + 1) * 10).astype(np.float16).view(np.uint16)
+    base_g = dev_f16(g)
+    base_16 = torch.zeros(n + 1, dtype=torch.float16, device="cuda")
+    d_w, d_v, d_g, d_16 = base_w[1:], base_v[1:], base_g[1:], base_16[1:]
+    h_w = host_f32(d_w).copy(); h_v = host_f32(d_v).copy(); h_g = g[1:].copy()
+    h_16 = np.zeros(n, np.uint16)
+    dS = mp.Scaler(4.0, False)
+    pl = mp.ParamList([d_w], [d_v], [d_g], [d_16])
+    mp.step(pl, dS, 0.01, 0.9, 1e-4)
+    oracle.step([h_w], [h_v], [h_g], [h_16], 0.01, 0.9, 1e-4, 0.25)
+    torch.cuda.synchronize()
+    assert same_f32_bits(host_f32(d_w), h_w) and same_f32_bits(host_f32(d_v), h_v)
+    assert same_f16_bits(host_bits16(d_16), h_16)
+    pl.close()
+
+
+def test_prechecked_flag_skips_the_check_pass():
+    """With MP_GRADS_PRECHECKED the sweep trusts found_inf: a clean flag updates, a set flag skips."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(3))
+    n = 30000
+    w = rng.standard_normal(n).astype(np.float32)
+    g = (rng.standard_normal(n)).astype(np.float16).view(np.uint16)
+    r = Run([w], [np.zeros(n, np.float32)], [g])
+    dS, oS = scaler_pair(1.0, True)
+    pl = r.plist()
+    mp.step(pl, dS, 0.01, 0.9, 0.0, flags=mp.MP_GRADS_PRECHECKED)
+    r.oracle_step(0.01, 0.9, 0.0, 1.0)
+    r.assert_equal()
+    before = host_f32(r.d_w[0]).copy()
+    dS.buf[4] = 1
+    mp.step(pl, dS, 0.01, 0.9, 0.0, flags=mp.MP_GRADS_PRECHECKED)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(r.d_w[0]), before)
+    pl.close()
+
+
+def test_determinism():
+    """Pin P10: the same inputs give the same bits twice."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(4))
+    sizes = [100003, 5]
+    outs = []
+    for _ in range(2):
+        r = Run([rng.standard_normal(n).astype(np.float32) * 0 + 1 for n in sizes],
+                [np.zeros(n, np.float32) for n in sizes],
+                [np.full(n, 0x3555, np.uint16) for n in sizes])
+        dS = mp.Scaler(2.0, True)
+        pl = r.plist()
+        for _ in range(3):
+            mp.step(pl, dS, 0.01, 0.9, 1e-4)
+        torch.cuda.synchronize()
+        outs.append([host_f32(t).copy() for t in r.d_w + r.d_v])
+        pl.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.timeout(900)
+def test_c2_update_sweep_full_size():
+    """C2: one flat tensor of 10^8 parameters, 50 steps, +inf injected at step 25, dynamic scaler.
+    The oracle runs its own trajectory from the same generated inputs; masters, momenta and binary16
+    copies are compared bit for bit after steps 0, 1, 24, 25, 26 and 49, on a fixed sample of
+    2^20 elements after every other step, and the scaler after every step."""
+    require_gpu()
+    cfg = workloads.c2()
+    n = cfg.w32.size
+    r = Run([cfg.w32], [np.zeros(n, np.float32)], [workloads.grads_at_scale(cfg.g_true, cfg.scale)])
+    dS, oS = scaler_pair(cfg.scale, cfg.dynamic, cfg.growth_interval)
+    pl = r.plist()
+    sample = np.random.Generator(np.random.PCG64(99)).choice(n, 1 << 20, replace=False)
+    g_scale = cfg.scale
+    for t in range(cfg.steps):
+        if oS.scale != g_scale or t == cfg.inf_step or t == cfg.inf_step + 1:
+            g_scale = oS.scale
+            g = workloads.grads_at_scale(cfg.g_true, g_scale)
+            if t == cfg.inf_step:
+                g[cfg.inf_index] = workloads.F16_INF
+            r.set_grads([g])
+        print(f"C2 step {t} scale {oS.scale}", flush=True)
+        mp.step(pl, dS, cfg.lr, cfg.momentum, cfg.weight_decay)
+        flag = r.oracle_step(cfg.lr, cfg.momentum, cfg.weight_decay, oS.inv_scale)
+        assert flag == (1 if t == cfg.inf_step else 0)
+        dS.update(); oracle.scaler_update(oS, flag)
+        assert_scaler(dS, oS)
+        if t in (0, 1, 24, 25, 26, cfg.steps - 1):
+            r.assert_equal(f"step {t}")
+        else:
+            torch.cuda.synchronize()
+            idx = torch.from_numpy(sample).cuda()
+            assert same_f32_bits(host_f32(r.d_w[0][idx]), r.h_w[0][sample]), t
+            assert same_f32_bits(host_f32(r.d_v[0][idx]), r.h_v[0][sample]), t
+    s = dS.read()
+    assert s["scale"] == 2.0 ** 14 and s["count"] == 24 and s["skipped_steps"] == 1
+    pl.close()

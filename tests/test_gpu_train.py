@@ -1,0 +1,109 @@
+"""End-to-end training steps through libmp against an independent oracle run.
+
+The 2-layer MLP 256 -> 512 -> 10 (ReLU, softmax cross-entropy, batch 64, static
+loss scale 1024, SGD lr 0.01 momentum 0.9, 10 steps) follows "Mixed Precision
+Training", long-form analysis page, §3.4 "The Integrated Training Procedure",
+Steps 1-7. The oracle never sees a GPU result: both sides start from the same
+generated inputs and run their own 10 steps; the losses must agree within 1e-2
+relative at every step (GEMM rounding differences compound, so the trajectory is
+compared with a tolerance, not bitwise).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_neural_amd as mp
+import oracle
+import workloads
+from gpu_util import dev_f16, dev_f32, host_f32, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_c1(cfg, steps, scale=None):
+    S = oracle.scaler_init(scale or cfg.scale, cfg.dynamic, cfg.growth_interval)
+    W = [cfg.W1.copy(), cfg.W2.copy()]
+    V = [np.zeros_like(W[0]), np.zeros_like(W[1])]
+    W16 = [oracle.f32_to_f16(w) for w in W]
+    G = [np.zeros(w.shape, np.uint16) for w in W]
+    losses, flags = [], []
+    for _ in range(steps):
+        Z1 = oracle.linear_fwd(cfg.X16, W16[0], out_f16=True)
+        H1 = oracle.relu_fwd(Z1)
+        Z2 = oracle.linear_fwd(H1, W16[1], out_f16=True)
+        loss, dZ2 = oracle.softmax_ce(Z2, cfg.labels, S.scale)
+        G[1][:] = oracle.linear_wgrad(dZ2, H1, out_f16=True)
+        dH1 = oracle.linear_dgrad(dZ2, W16[1], out_f16=True)
+        dZ1 = oracle.relu_bwd(Z1, dH1)
+        G[0][:] = oracle.linear_wgrad(dZ1, cfg.X16, out_f16=True)
+        f = oracle.step([W[0].reshape(-1), W[1].reshape(-1)], [V[0].reshape(-1), V[1].reshape(-1)],
+                        [G[0].reshape(-1), G[1].reshape(-1)], [W16[0].reshape(-1), W16[1].reshape(-1)],
+                        cfg.lr, cfg.momentum, cfg.weight_decay, S.inv_scale)
+        oracle.scaler_update(S, f)
+        losses.append(loss); flags.append(f)
+    return losses, flags, W, S
+
+
+def gpu_c1(cfg, steps, scale=None):
+    S = mp.Scaler(scale or cfg.scale, cfg.dynamic, cfg.growth_interval)
+    W = [dev_f32(cfg.W1), dev_f32(cfg.W2)]
+    V = [torch.zeros_like(w) for w in W]
+    W16 = [mp.round_f32_to_f16(w) for w in W]
+    G = [torch.zeros(w.shape, dtype=torch.float16, device="cuda") for w in W]
+    pl = mp.ParamList(W, V, G, W16)
+    X = dev_f16(cfg.X16)
+    y = torch.from_numpy(cfg.labels).cuda()
+    Z1 = torch.empty((64, 512), dtype=torch.float16, device="cuda")
+    H1, dH1, dZ1 = torch.empty_like(Z1), torch.empty_like(Z1), torch.empty_like(Z1)
+    Z2 = torch.empty((64, 10), dtype=torch.float16, device="cuda")
+    dZ2 = torch.empty_like(Z2)
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    losses, flags = [], []
+    for _ in range(steps):
+        mp.linear_fwd(X, W16[0], Y=Z1)
+        mp.act_fwd(mp.RELU, Z1, H1)
+        mp.linear_fwd(H1, W16[1], Y=Z2)
+        mp.loss_softmax_ce(Z2, y, S, loss, dZ2)
+        mp.linear_wgrad(dZ2, H1, dW=G[1])
+        mp.linear_dgrad(dZ2, W16[1], dX=dH1)
+        mp.act_bwd(mp.RELU, Z1, dH1, dZ1)
+        mp.linear_wgrad(dZ1, X, dW=G[0])
+        mp.step(pl, S, cfg.lr, cfg.momentum, cfg.weight_decay)
+        flags.append(S.read()["found_inf"])
+        S.update()
+        losses.append(float(loss.item()))
+    torch.cuda.synchronize()
+    out = [host_f32(w) for w in W], S.read()
+    pl.close()
+    return losses, flags, out
+
+
+def test_c1_ten_steps_match_independent_oracle_run():
+    """Pin P12: per-step loss within 1e-2 relative; final masters close; no step skipped."""
+    require_gpu()
+    cfg = workloads.c1()
+    o_loss, o_flags, o_W, o_S = oracle_c1(cfg, cfg.steps)
+    g_loss, g_flags, (g_W, g_S) = gpu_c1(cfg, cfg.steps)
+    print("oracle", [round(x, 5) for x in o_loss], flush=True)
+    print("gpu   ", [round(x, 5) for x in g_loss], flush=True)
+    for t, (a, b) in enumerate(zip(g_loss, o_loss)):
+        assert math.isclose(a, b, rel_tol=1e-2), (t, a, b)
+    assert o_loss[-1] < o_loss[0]                    # it trains
+    assert g_flags == o_flags == [0] * cfg.steps
+    for gw, ow in zip(g_W, o_W):
+        assert np.max(np.abs(gw - ow)) <= 1e-3 * max(1.0, np.max(np.abs(ow)))
+    assert g_S["scale"] == o_S.scale == 1024.0
+
+
+def test_c1_absurd_scale_overflows_and_skips():
+    """A loss scale of 2^40 overflows the scaled loss gradient to inf in binary16; the inf reaches
+    the weight gradients, every step is skipped and the static scale stays (method 1)."""
+    require_gpu()
+    cfg = workloads.c1()
+    o_loss, o_flags, o_W, o_S = oracle_c1(cfg, 2, scale=2.0 ** 40)
+    g_loss, g_flags, (g_W, g_S) = gpu_c1(cfg, 2, scale=2.0 ** 40)
+    assert o_flags == g_flags == [1, 1]
+    assert np.array_equal(g_W[0], cfg.W1) and np.array_equal(g_W[1], cfg.W2)
+    assert g_S["skipped_steps"] == o_S.skipped_steps == 2 and g_S["scale"] == 2.0 ** 40
