@@ -15,14 +15,24 @@
 //   wgrad    dW = dY^T X : A = dY (MN), B = X (MN), reduction over M
 //
 // Per block: a BM x BN output tile, BK = 64 reduction slices staged through
-// LDS in two buffers. Both operands are stored in LDS the same way, as rows of
-// 64 reduction elements (128 bytes, eight 16-byte chunks, XOR-swizzled by row
-// to keep the MFMA fragment reads free of bank conflicts). A KC operand is
-// copied as 16-byte vectors; an MN operand is loaded as 8 x 8 blocks of
-// 16-byte vectors and transposed in registers before it is written, so the
-// inner loop is the same for all three layouts. Each wave owns a
-// (BM / WAVES_M) x (BN / WAVES_N) sub-tile of 32 x 32 MFMA tiles
-// (v_mfma_f32_32x32x16_f16: binary16 inputs, exact products, FP32 sums).
+// LDS in two buffers; the next slice's global loads are in flight while the
+// current slice feeds the MFMAs (v_mfma_f32_32x32x16_f16: binary16 inputs,
+// exact products, FP32 sums). Each operand keeps its global layout in LDS, so
+// every global load and LDS store is a plain 16-byte vector:
+//   KC tile: ROWS rows of 64 reduction elements (128 bytes, 8 chunks of 16
+//     bytes), chunk c of row r at r*8 + (c ^ ((r ^ r>>3) & 7)); an MFMA
+//     fragment row is one ds_read_b128.
+//   MN tile: 64 reduction rows of ROWS index elements, chunk c of row k at
+//     k*ROWS/8 + (c ^ (4*(k & 3) mod ROWS/8)); an MFMA fragment is two
+//     ds_read_b64_tr_b16, whose lane j of each 16-lane group collects element j
+//     of the four 8-byte pieces its group reads, i.e. four reduction values of
+//     one index column.
+// Both swizzles keep the fragment reads of the 256-wide tiles free of LDS bank
+// conflicts. For whole tiles the steady-state slice loop has no branches and
+// an explicit instruction order: in sub-step 0 every MFMA is paired with a
+// global load, in sub-steps 0-2 with the LDS reads of the next sub-step, in
+// sub-step 3 with an LDS store of the next slice, so memory traffic issues
+// while the matrix cores run instead of between their bursts.
 // Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
 // 8 XCDs) works on a compact group of tiles that share rows of A and B in its
 // own L2.
@@ -32,9 +42,12 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 constexpr int kBK = 64;          // reduction slice per LDS stage
-constexpr int kRowChunks = 8;    // 16-byte chunks per LDS row (64 binary16)
+constexpr int kRowChunks = 8;    // 16-byte chunks per KC row (64 binary16)
 
 struct GemmArgs {
     const uint16_t* A;
@@ -47,60 +60,64 @@ struct GemmArgs {
     int tiles_m, tiles_n;
 };
 
-// Physical 16-byte chunk of logical chunk `c` in LDS row `row`.
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
+__device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
+template <int CHUNKS>
+__device__ __forceinline__ int swz_mn(int krow) { return ((krow & 3) << 2) & (CHUNKS - 1); }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
-// Loads 8 consecutive binary16 values p[0..7], of which only the first `valid`
-// exist (valid may be <= 0). `vec` allows one 16-byte load when all 8 exist.
-__device__ __forceinline__ uint4 load8(const uint16_t* p, int64_t valid, int vec) {
-    if (vec && valid >= 8) return *reinterpret_cast<const uint4*>(p);
-    uint16_t t[8];
+// Loads of 8 consecutive binary16 values p[0..7]. The edge version never
+// branches: every element is read through a clamped (always valid) address and
+// zeroed afterwards when it lies outside [0, valid), so the loads of a tile
+// stay in flight together instead of waiting one by one.
+__device__ __forceinline__ uint4 load8_full(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint4 load8_edge(const uint16_t* p, const uint16_t* safe, int64_t valid) {
+    uint32_t t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = (i < valid) ? p[i] : uint16_t(0);
-    return make_uint4(uint32_t(t[0]) | uint32_t(t[1]) << 16, uint32_t(t[2]) | uint32_t(t[3]) << 16,
-                      uint32_t(t[4]) | uint32_t(t[5]) << 16, uint32_t(t[6]) | uint32_t(t[7]) << 16);
+    for (int i = 0; i < 8; ++i) {
+        const bool ok = i < valid;
+        const uint16_t v = *(ok ? p + i : safe);
+        t[i] = ok ? uint32_t(v) : 0u;
+    }
+    return make_uint4(t[0] | t[1] << 16, t[2] | t[3] << 16, t[4] | t[5] << 16, t[6] | t[7] << 16);
 }
 
-__device__ __forceinline__ uint32_t half_of(const uint4& v, int j) {
-    const uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
-    return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
-// A tile of one operand in flight between global memory and LDS.
+// One operand's tile (ROWS index rows x 64 reduction elements) in flight from
+// global memory to LDS: ROWS * 8 chunks of 16 bytes, kPer per thread.
 template <int ROWS, int NT, bool KC>
 struct TileLoader {
-    // KC: ROWS*8 chunks of 16 bytes; MN: ROWS 8x8 blocks of 8 chunks each.
-    static constexpr int kItems = KC ? (ROWS * kRowChunks) : ROWS;
-    static constexpr int kPer = (kItems + NT - 1) / NT;
-    static constexpr int kRegs = KC ? kPer : kPer * 8;
-    uint4 r[kRegs];
+    static constexpr int kItems = ROWS * kRowChunks;
+    static constexpr int kPer = kItems / NT;
+    static constexpr int kMnChunks = ROWS / 8;       // chunks per MN row
+    static_assert(kItems % NT == 0, "threads must divide the tile");
+    uint4 r[kPer];
 
-    // Rows of the tile are [row0, row0 + ROWS) of the operand's "index" space,
-    // the reduction slice is [k0, k0 + 64).
+    // FULL: the whole tile is in bounds and 16-byte loads are allowed.
+    template <bool FULL>
     __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int64_t rows_total,
-                                         int64_t R, int64_t row0, int64_t k0, int vec, int tid) {
+                                         int64_t R, int64_t row0, int64_t k0, int tid) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int q = tid + u * NT;
             if (KC) {
                 const int row = q / kRowChunks, kc = q % kRowChunks;
                 const int64_t gr = row0 + row, gk = k0 + kc * 8;
-                if (q < kItems && gr < rows_total)
-                    r[u] = load8(base + gr * ld + gk, R - gk, vec);
-                else
-                    r[u] = zero4();
+                if (FULL) {
+                    r[u] = load8_full(base + gr * ld + gk);
+                } else {
+                    const bool ok = gr < rows_total;
+                    r[u] = load8_edge(base + (ok ? gr : 0) * ld + gk, base, ok ? R - gk : 0);
+                }
             } else {
-                const int mb = q % (ROWS / 8), rb = q / (ROWS / 8);
-                const int64_t gm = row0 + mb * 8;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int64_t gk = k0 + rb * 8 + i;
-                    if (q < kItems && gk < R)
-                        r[u * 8 + i] = load8(base + gk * ld + gm, rows_total - gm, vec);
-                    else
-                        r[u * 8 + i] = zero4();
+                const int k = q / kMnChunks, cb = q % kMnChunks;
+                const int64_t gk = k0 + k, gm = row0 + cb * 8;
+                if (FULL) {
+                    r[u] = load8_full(base + gk * ld + gm);
+                } else {
+                    const bool ok = gk < R;
+                    r[u] = load8_edge(base + (ok ? gk : 0) * ld + gm, base, ok ? rows_total - gm : 0);
                 }
             }
         }
@@ -110,38 +127,138 @@ struct TileLoader {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int q = tid + u * NT;
-            if (q >= kItems) continue;
             if (KC) {
                 const int row = q / kRowChunks, kc = q % kRowChunks;
-                lds[row * kRowChunks + swz(row, kc)] = r[u];
+                lds[row * kRowChunks + (kc ^ swz_kc(row))] = r[u];
             } else {
-                const int mb = q % (ROWS / 8), rb = q / (ROWS / 8);
-                // r[u*8 + i] holds 8 consecutive index-space values at reduction
-                // offset rb*8 + i; row j of the LDS tile wants the 8 reduction
-                // values of index mb*8 + j.
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint4* in = &r[u * 8];
-                    uint4 o;
-                    o.x = half_of(in[0], j) | (half_of(in[1], j) << 16);
-                    o.y = half_of(in[2], j) | (half_of(in[3], j) << 16);
-                    o.z = half_of(in[4], j) | (half_of(in[5], j) << 16);
-                    o.w = half_of(in[6], j) | (half_of(in[7], j) << 16);
-                    const int row = mb * 8 + j;
-                    lds[row * kRowChunks + swz(row, rb)] = o;
-                }
+                const int k = q / kMnChunks, cb = q % kMnChunks;
+                lds[k * kMnChunks + (cb ^ swz_mn<kMnChunks>(k))] = r[u];
             }
         }
     }
 };
 
+// MFMA fragment of index rows [r0, r0 + 32) for reduction sub-step kk (16
+// values) from one operand's LDS tile of ROWS index rows: lane l holds index
+// r0 + (l & 31) and the 8 reduction values 16*kk + 8*(l >> 5) .. + 7.
+template <int ROWS, bool KC>
+__device__ __forceinline__ half8 frag(const uint4* tile, int r0, int kk, int lane) {
+    if (KC) {
+        const int row = r0 + (lane & 31);
+        const int c = 2 * kk + (lane >> 5);
+        return __builtin_bit_cast(half8, tile[row * kRowChunks + (c ^ swz_kc(row))]);
+    } else {
+        constexpr int kMnChunks = ROWS / 8;
+        const int g4 = lane >> 4, ii = lane & 15;
+        const int n = r0 + 16 * (g4 & 1) + 4 * (ii & 3);
+        short4_t v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int krow = 16 * kk + 8 * (g4 >> 1) + 4 * h + (ii >> 2);
+            const int chunk = krow * kMnChunks + ((n >> 3) ^ swz_mn<kMnChunks>(krow));
+            const __attribute__((address_space(3))) uint8_t* p =
+                (const __attribute__((address_space(3))) uint8_t*)(tile + chunk) + ((n >> 2) & 1) * 8;
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p));
+        }
+        const short8_t w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+        return __builtin_bit_cast(half8, w);
+    }
+}
+
+// The reduction loop of one block.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, bool FULL, int FM, int FN>
+__device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64_t row0, int64_t col0,
+                                            int tid, int lane, int wm, int wn,
+                                            floatx16 (&acc)[FM][FN]) {
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int kStage = (BM + BN) * kRowChunks;   // uint4 per LDS stage
+    TileLoader<BM, NT, A_KC> la;
+    TileLoader<BN, NT, B_KC> lb;
+    const int nk = int((g.R + kBK - 1) / kBK);
+    if (nk <= 0) return;
+    la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, 0, tid);
+    lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, 0, tid);
+    la.store(lds, tid);
+    lb.store(lds + BM * kRowChunks, tid);
+    __syncthreads();
+
+    auto read_frags = [&](const uint4* st, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = frag<BM, A_KC>(st, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = frag<BN, B_KC>(st + BM * kRowChunks, wn * WTN + j * 32, kk, lane);
+    };
+    // All four sub-steps of one slice, with the fragments of sub-step kk+1
+    // read while the MFMAs of sub-step kk run.
+    auto slice = [&](const uint4* st) {
+        half8 af[2][FM], bf[2][FN];
+        read_frags(st, 0, af[0], bf[0]);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int c = kk & 1;
+            if (kk + 1 < kBK / 16) read_frags(st, kk + 1, af[c ^ 1], bf[c ^ 1]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    int kt = 0;
+    if (FULL && FM * FN == 16 && TileLoader<BM, NT, A_KC>::kPer + TileLoader<BN, NT, B_KC>::kPer == 16) {
+        // Steady state: every slice but the last, one basic block per slice.
+        constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per sub-step
+        static_assert(kReads <= 16, "at most one LDS read per MFMA");
+        for (; kt + 1 < nk; ++kt) {
+            const int cur = kt & 1;
+            const int64_t k0 = int64_t(kt + 1) * kBK;
+            la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, k0, tid);
+            lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, k0, tid);
+            slice(lds + cur * kStage);
+            uint4* nxt = lds + (cur ^ 1) * kStage;
+            la.store(nxt, tid);
+            lb.store(nxt + BM * kRowChunks, tid);
+            // Instruction order of the slice (groups are filled in program order).
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);            // sub-step 0 fragments
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                    if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // global load
+                    if (kk < 3 && m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    if (kk == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);            // LDS store
+                }
+            __syncthreads();
+        }
+    }
+    for (; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int64_t k0 = int64_t(kt + 1) * kBK;
+            la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, k0, tid);
+            lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, k0, tid);
+        }
+        slice(lds + cur * kStage);
+        if (more) {
+            uint4* nxt = lds + (cur ^ 1) * kStage;
+            la.store(nxt, tid);
+            lb.store(nxt + BM * kRowChunks, tid);
+        }
+        __syncthreads();
+    }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, bool OUT_F16>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArgs g) {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int kStage = (BM + BN) * kRowChunks;         // uint4 per LDS stage
     __shared__ uint4 lds[2 * kStage];
+    static_assert(BM % 32 == 0 && BN % 32 == 0, "tile must be whole MFMA tiles");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -160,9 +277,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
     const int tn = (lb % per_group) / gsize;
     const int64_t row0 = int64_t(tm) * BM, col0 = int64_t(tn) * BN;
 
-    TileLoader<BM, NT, A_KC> la;
-    TileLoader<BN, NT, B_KC> lb_;
-
     floatx16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -171,50 +285,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = int((g.R + kBK - 1) / kBK);
-    if (nk > 0) {
-        la.load(g.A, g.lda, g.Mc, g.R, row0, 0, g.a_vec, tid);
-        lb_.load(g.B, g.ldb, g.Nc, g.R, col0, 0, g.b_vec, tid);
-        la.store(lds, tid);
-        lb_.store(lds + BM * kRowChunks, tid);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const int64_t k0 = int64_t(kt + 1) * kBK;
-            la.load(g.A, g.lda, g.Mc, g.R, row0, k0, g.a_vec, tid);
-            lb_.load(g.B, g.ldb, g.Nc, g.R, col0, k0, g.b_vec, tid);
-        }
-        const uint4* sA = lds + cur * kStage;
-        const uint4* sB = sA + BM * kRowChunks;
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int chunk = 2 * kk + (lane >> 5);
-            half8 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * WTM + i * 32 + (lane & 31);
-                af[i] = __builtin_bit_cast(half8, sA[row * kRowChunks + swz(row, chunk)]);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * WTN + j * 32 + (lane & 31);
-                bf[j] = __builtin_bit_cast(half8, sB[row * kRowChunks + swz(row, chunk)]);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            uint4* nA = lds + (cur ^ 1) * kStage;
-            la.store(nA, tid);
-            lb_.store(nA + BM * kRowChunks, tid);
-        }
-        __syncthreads();
-    }
+    const bool full = g.a_vec && g.b_vec && (g.R % kBK) == 0 && row0 + BM <= g.Mc &&
+                      col0 + BN <= g.Nc;
+    if (full)
+        reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, true, FM, FN>(g, lds, row0, col0, tid, lane,
+                                                                      wm, wn, acc);
+    else
+        reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, false, FM, FN>(g, lds, row0, col0, tid, lane,
+                                                                       wm, wn, acc);
 
     // ---- epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
     uint32_t bad = 0;

@@ -40,9 +40,12 @@ def gpu_all(X, W, dY, out=torch.float32):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (64, 10, 32), (17, 300, 24), (300, 257, 32),
-                                   (2600, 3100, 32)])
+                                   (2600, 3100, 32), (512, 768, 256), (1024, 512, 1536)])
 def test_exact_integer_sums(M, N, K):
-    """Pin P8: on a 2^-q grid with |x| <= 2 every product is a multiple of 2^-2q below 4, so a
+    """Shapes whose tiles are all whole (multiples of 256, reductions multiples of 128) take the
+    direct-to-LDS kernel; the others the general kernel.
+
+    Pin P8: on a 2^-q grid with |x| <= 2 every product is a multiple of 2^-2q below 4, so a
     partial sum over R terms is a multiple of 2^-2q below 4R: exact in FP32 while 4R * 2^2q <= 2^24.
     The GPU result must then equal the integer sum bit for bit in any summation order. q = 8 for
     reductions up to 32, q = 4 up to 4096 (both tile paths)."""
@@ -88,7 +91,8 @@ def test_fp32_accumulation_discriminator():
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 512, 256), (64, 10, 512), (300, 520, 200), (777, 1000, 333),
-                                   (2600, 3100, 96), (4099, 2050, 130)])
+                                   (2600, 3100, 96), (4099, 2050, 130), (512, 768, 256),
+                                   (1280, 1024, 384)])
 def test_ragged_shapes_against_oracle(M, N, K):
     """Shapes spanning several tiles with ragged edges in every dimension, FP32 and binary16 out."""
     require_gpu()
