@@ -276,3 +276,80 @@ def test_c2_update_sweep_full_size():
     s = dS.read()
     assert s["scale"] == 2.0 ** 14 and s["count"] == 24 and s["skipped_steps"] == 1
     pl.close()
+
+
+@pytest.mark.timeout(1500)
+def test_c5_ragged_step_full_size():
+    """C5: 500 tensors with log-uniform sizes summing to 1.5e9 parameters, lr 1e-3, momentum 0.9,
+    weight decay 1e-4, dynamic scale from 2^12, 0.1 % NaN injected at step 7, 20 steps. The oracle
+    runs its own 20 steps from the same generated inputs; masters, momenta and binary16 copies are
+    compared bit for bit in full after steps 0, 6, 7, 8 and 19 and on a fixed sample of 2^20
+    elements per step otherwise; the scaler after every step."""
+    import concurrent.futures as cf
+
+    require_gpu()
+    hp = workloads.C5Hyper()
+    sizes = workloads.c5_sizes()
+    total = int(sizes.sum())
+    first = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    print(f"C5 generating {sizes.size} tensors, {total} parameters", flush=True)
+    with cf.ThreadPoolExecutor(16) as ex:
+        tens = list(ex.map(lambda a: workloads.c5_tensor(a[0], a[1]), enumerate(sizes)))
+    nan_idx = workloads.c5_nan_indices(total)
+    nan_t = np.searchsorted(first, nan_idx, side="right") - 1
+    h_w = [t.w32 for t in tens]
+    h_v = [np.zeros(s, np.float32) for s in sizes]
+    h_16 = [oracle.f32_to_f16(w) for w in h_w]
+    h_g = [np.empty(s, np.uint16) for s in sizes]
+    d_w = [dev_f32(w) for w in h_w]
+    d_v = [torch.zeros(int(s), dtype=torch.float32, device="cuda") for s in sizes]
+    d_g = [torch.empty(int(s), dtype=torch.float16, device="cuda") for s in sizes]
+    d_16 = [mp.round_f32_to_f16(w) for w in d_w]
+    pl = mp.ParamList(d_w, d_v, d_g, d_16)
+    dS, oS = scaler_pair(hp.scale, hp.dynamic, hp.growth_interval)
+    rng = np.random.Generator(np.random.PCG64(55))
+    samp_t = rng.integers(0, sizes.size, 1 << 20)
+    samp_i = (rng.random(1 << 20) * sizes[samp_t]).astype(np.int64)
+
+    def set_grads(scale, inject):
+        def one(t):
+            g = workloads.grads_at_scale(tens[t].g_true, scale)
+            if inject:
+                sel = nan_idx[nan_t == t] - first[t]
+                g[sel] = workloads.F16_QNAN
+            h_g[t][:] = g
+            d_g[t].copy_(torch.from_numpy(g.view(np.int16)).view(torch.float16))
+        with cf.ThreadPoolExecutor(8) as ex:
+            list(ex.map(one, range(sizes.size)))
+
+    def full_compare(step):
+        torch.cuda.synchronize()
+        for t in range(sizes.size):
+            assert same_f32_bits(host_f32(d_w[t]), h_w[t]), (step, t)
+            assert same_f32_bits(host_f32(d_v[t]), h_v[t]), (step, t)
+            assert same_f16_bits(host_bits16(d_16[t]), h_16[t]), (step, t)
+
+    g_scale = None
+    for step in range(hp.steps):
+        inject = step == hp.nan_step
+        if oS.scale != g_scale or inject or step == hp.nan_step + 1:
+            g_scale = oS.scale
+            set_grads(g_scale, inject)
+        print(f"C5 step {step} scale {oS.scale}", flush=True)
+        mp.step(pl, dS, hp.lr, hp.momentum, hp.weight_decay)
+        flag = oracle.step(h_w, h_v, h_g, h_16, hp.lr, hp.momentum, hp.weight_decay, oS.inv_scale)
+        assert flag == (1 if inject else 0)
+        dS.update(); oracle.scaler_update(oS, flag)
+        assert_scaler(dS, oS)
+        if step in (0, hp.nan_step - 1, hp.nan_step, hp.nan_step + 1, hp.steps - 1):
+            full_compare(step)
+        else:
+            torch.cuda.synchronize()
+            for t in np.unique(samp_t)[:64]:
+                sel = samp_i[samp_t == t]
+                idx = torch.from_numpy(sel).cuda()
+                assert same_f32_bits(host_f32(d_w[t][idx]), h_w[t][sel]), (step, t)
+                assert same_f32_bits(host_f32(d_v[t][idx]), h_v[t][sel]), (step, t)
+    s = dS.read()
+    assert s["scale"] == 2.0 ** 11 and s["count"] == 12 and s["skipped_steps"] == 1
+    pl.close()

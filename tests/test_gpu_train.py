@@ -46,7 +46,9 @@ def oracle_c1(cfg, steps, scale=None):
     return losses, flags, W, S
 
 
-def gpu_c1(cfg, steps, scale=None):
+def gpu_c1(cfg, steps, scale=None, prechecked=False):
+    """prechecked: the weight-gradient GEMMs set the scaler's overflow flag in their epilogue and
+    the sweep skips its own check pass (Step 6 fused into the producer)."""
     S = mp.Scaler(scale or cfg.scale, cfg.dynamic, cfg.growth_interval)
     W = [dev_f32(cfg.W1), dev_f32(cfg.W2)]
     V = [torch.zeros_like(w) for w in W]
@@ -66,11 +68,13 @@ def gpu_c1(cfg, steps, scale=None):
         mp.act_fwd(mp.RELU, Z1, H1)
         mp.linear_fwd(H1, W16[1], Y=Z2)
         mp.loss_softmax_ce(Z2, y, S, loss, dZ2)
-        mp.linear_wgrad(dZ2, H1, dW=G[1])
+        fi = S.found_inf_ptr if prechecked else None
+        mp.linear_wgrad(dZ2, H1, dW=G[1], found_inf=fi)
         mp.linear_dgrad(dZ2, W16[1], dX=dH1)
         mp.act_bwd(mp.RELU, Z1, dH1, dZ1)
-        mp.linear_wgrad(dZ1, X, dW=G[0])
-        mp.step(pl, S, cfg.lr, cfg.momentum, cfg.weight_decay)
+        mp.linear_wgrad(dZ1, X, dW=G[0], found_inf=fi)
+        mp.step(pl, S, cfg.lr, cfg.momentum, cfg.weight_decay,
+                flags=mp.MP_GRADS_PRECHECKED if prechecked else 0)
         flags.append(S.read()["found_inf"])
         S.update()
         losses.append(float(loss.item()))
@@ -80,12 +84,13 @@ def gpu_c1(cfg, steps, scale=None):
     return losses, flags, out
 
 
-def test_c1_ten_steps_match_independent_oracle_run():
+@pytest.mark.parametrize("prechecked", [False, True])
+def test_c1_ten_steps_match_independent_oracle_run(prechecked):
     """Pin P12: per-step loss within 1e-2 relative; final masters close; no step skipped."""
     require_gpu()
     cfg = workloads.c1()
     o_loss, o_flags, o_W, o_S = oracle_c1(cfg, cfg.steps)
-    g_loss, g_flags, (g_W, g_S) = gpu_c1(cfg, cfg.steps)
+    g_loss, g_flags, (g_W, g_S) = gpu_c1(cfg, cfg.steps, prechecked=prechecked)
     print("oracle", [round(x, 5) for x in o_loss], flush=True)
     print("gpu   ", [round(x, 5) for x in g_loss], flush=True)
     for t, (a, b) in enumerate(zip(g_loss, o_loss)):
@@ -97,13 +102,14 @@ def test_c1_ten_steps_match_independent_oracle_run():
     assert g_S["scale"] == o_S.scale == 1024.0
 
 
-def test_c1_absurd_scale_overflows_and_skips():
+@pytest.mark.parametrize("prechecked", [False, True])
+def test_c1_absurd_scale_overflows_and_skips(prechecked):
     """A loss scale of 2^40 overflows the scaled loss gradient to inf in binary16; the inf reaches
     the weight gradients, every step is skipped and the static scale stays (method 1)."""
     require_gpu()
     cfg = workloads.c1()
     o_loss, o_flags, o_W, o_S = oracle_c1(cfg, 2, scale=2.0 ** 40)
-    g_loss, g_flags, (g_W, g_S) = gpu_c1(cfg, 2, scale=2.0 ** 40)
+    g_loss, g_flags, (g_W, g_S) = gpu_c1(cfg, 2, scale=2.0 ** 40, prechecked=prechecked)
     assert o_flags == g_flags == [1, 1]
     assert np.array_equal(g_W[0], cfg.W1) and np.array_equal(g_W[1], cfg.W2)
     assert g_S["skipped_steps"] == o_S.skipped_steps == 2 and g_S["scale"] == 2.0 ** 40
