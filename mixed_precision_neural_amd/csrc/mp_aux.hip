@@ -21,32 +21,8 @@ constexpr int kThreads = 256;
 constexpr int kMaxPartials = 1024;
 __device__ float g_partials[kMaxPartials];
 
-constexpr float kInvSqrt2 = 0.70710678118654752440f;
-constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
-
-// Phi(x) = (1 + erf(x / sqrt 2)) / 2 is evaluated as erfc(-x / sqrt 2) / 2: for negative x
-// the sum 1 + erf cancels and would leave only a few correct bits in FP32.
-__device__ __forceinline__ float std_normal_cdf(float x) { return 0.5f * erfcf(-x * kInvSqrt2); }
-__device__ __forceinline__ float gelu_f(float x) { return x * std_normal_cdf(x); }
-__device__ __forceinline__ float gelu_d(float x) {
-    return std_normal_cdf(x) + x * kInvSqrt2Pi * expf(-0.5f * x * x);
-}
-
-template <int KIND>
-__device__ __forceinline__ uint16_t act_fwd1(uint16_t xh) {
-    if (KIND == MP_ACT_RELU) {
-        const float x = mp::h2f(xh);
-        return (x > 0.0f || x != x) ? xh : uint16_t(0);
-    }
-    return mp::f2h(gelu_f(mp::h2f(xh)));
-}
-
-template <int KIND>
-__device__ __forceinline__ uint16_t act_bwd1(uint16_t xh, uint16_t dyh) {
-    const float x = mp::h2f(xh);
-    if (KIND == MP_ACT_RELU) return x > 0.0f ? dyh : uint16_t(0);
-    return mp::f2h(mp::h2f(dyh) * gelu_d(x));
-}
+using mp::act_bwd1;
+using mp::act_fwd1;
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }

@@ -60,6 +60,10 @@ struct GemmArgs {
     int tiles_m, tiles_n;
 };
 
+// Epilogue modes.
+constexpr int kEpiF32 = 0;       // C = acc (FP32)
+constexpr int kEpiF16 = 1;       // C = RNE16(acc)
+
 __device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
 template <int CHUNKS>
 __device__ __forceinline__ int swz_mn(int krow) { return ((krow & 3) << 2) & (CHUNKS - 1); }
@@ -252,7 +256,7 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, bool OUT_F16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArgs g) {
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -306,40 +310,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
                 const int64_t gr =
                     row0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (gr < g.Mc && gc < g.Nc) {
-                    if (OUT_F16) {
+                    if (EPI == kEpiF32) {
+                        static_cast<float*>(g.C)[gr * g.ldc + gc] = acc[i][j][r];
+                    } else {
                         const uint16_t h = mp::f2h(acc[i][j][r]);
                         bad |= mp::nonfinite1(h);
                         static_cast<uint16_t*>(g.C)[gr * g.ldc + gc] = h;
-                    } else {
-                        static_cast<float*>(g.C)[gr * g.ldc + gc] = acc[i][j][r];
                     }
                 }
             }
         }
-    if (OUT_F16 && g.flag) {
+    if (EPI == kEpiF16 && g.flag) {
         if (__syncthreads_or(bad) && tid == 0) atomicOr(g.flag, 1u);
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool A_KC, bool B_KC>
-mp_status launch_cfg(GemmArgs a, bool f16, hipStream_t s, const char* name) {
+template <int BM, int BN, int WM, int WN, bool A_KC, bool B_KC, int EPI>
+mp_status launch_cfg(GemmArgs a, hipStream_t s, const char* name) {
     a.tiles_m = int((a.Mc + BM - 1) / BM);
     a.tiles_n = int((a.Nc + BN - 1) / BN);
     const uint32_t blocks = uint32_t(a.tiles_m) * uint32_t(a.tiles_n);
-    if (f16)
-        gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, true><<<blocks, 64 * WM * WN, 0, s>>>(a);
-    else
-        gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, false><<<blocks, 64 * WM * WN, 0, s>>>(a);
+    gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, EPI><<<blocks, 64 * WM * WN, 0, s>>>(a);
     return mp::launch_status(name);
 }
 
-template <bool A_KC, bool B_KC>
-mp_status launch(GemmArgs a, bool f16, hipStream_t s, const char* name) {
+template <bool A_KC, bool B_KC, int EPI>
+mp_status launch(GemmArgs a, hipStream_t s, const char* name) {
     // Large outputs: 256 x 256 tiles, 4 waves of 128 x 128. Small outputs
     // (where a 256 x 256 grid would leave most of the 256 CUs idle): 64 x 64.
     const int64_t big_tiles = ((a.Mc + 255) / 256) * ((a.Nc + 255) / 256);
-    if (big_tiles >= 128) return launch_cfg<256, 256, 2, 2, A_KC, B_KC>(a, f16, s, name);
-    return launch_cfg<64, 64, 2, 2, A_KC, B_KC>(a, f16, s, name);
+    if (big_tiles >= 128) return launch_cfg<256, 256, 2, 2, A_KC, B_KC, EPI>(a, s, name);
+    return launch_cfg<64, 64, 2, 2, A_KC, B_KC, EPI>(a, s, name);
 }
 
 bool bad_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld) {
@@ -368,7 +369,9 @@ extern "C" mp_status mp_linear_fwd(const uint16_t* X, int64_t ldx, const uint16_
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(M, N)) return MP_ERR_INVALID_ARGUMENT;
     GemmArgs a{X, W, Y, ldx, ldw, ldy, M, N, K, nullptr, vec_ok(X, ldx), vec_ok(W, ldw), 0, 0};
-    return launch<true, true>(a, y_dtype == MP_F16, mp::as_stream(stream), "mp_linear_fwd");
+    hipStream_t s = mp::as_stream(stream);
+    if (y_dtype == MP_F16) return launch<true, true, kEpiF16>(a, s, "mp_linear_fwd");
+    return launch<true, true, kEpiF32>(a, s, "mp_linear_fwd");
 }
 
 extern "C" mp_status mp_linear_dgrad(const uint16_t* dY, int64_t lddy, const uint16_t* W,
@@ -381,7 +384,9 @@ extern "C" mp_status mp_linear_dgrad(const uint16_t* dY, int64_t lddy, const uin
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(M, K)) return MP_ERR_INVALID_ARGUMENT;
     GemmArgs a{dY, W, dX, lddy, ldw, lddx, M, K, N, nullptr, vec_ok(dY, lddy), vec_ok(W, ldw), 0, 0};
-    return launch<true, false>(a, dx_dtype == MP_F16, mp::as_stream(stream), "mp_linear_dgrad");
+    hipStream_t s = mp::as_stream(stream);
+    if (dx_dtype == MP_F16) return launch<true, false, kEpiF16>(a, s, "mp_linear_dgrad");
+    return launch<true, false, kEpiF32>(a, s, "mp_linear_dgrad");
 }
 
 extern "C" mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uint16_t* X,
@@ -396,5 +401,7 @@ extern "C" mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uin
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(N, K)) return MP_ERR_INVALID_ARGUMENT;
     GemmArgs a{dY, X, dW, lddy, ldx, lddw, N, K, M, found_inf, vec_ok(dY, lddy), vec_ok(X, ldx), 0, 0};
-    return launch<false, false>(a, dw_dtype == MP_F16, mp::as_stream(stream), "mp_linear_wgrad");
+    hipStream_t s = mp::as_stream(stream);
+    if (dw_dtype == MP_F16) return launch<false, false, kEpiF16>(a, s, "mp_linear_wgrad");
+    return launch<false, false, kEpiF32>(a, s, "mp_linear_wgrad");
 }

@@ -54,4 +54,31 @@ __device__ __forceinline__ uint32_t nonfinite1(uint16_t h) {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---- point-wise activations on binary16 values (shared by the stand-alone
+// kernels and the fused GEMM epilogues, so both produce the same bits) -------
+// GELU(x) = x * Phi(x) with the exact error function; Phi(x) is evaluated as
+// erfc(-x / sqrt 2) / 2 because 1 + erf(x / sqrt 2) cancels for negative x.
+__device__ __forceinline__ float std_normal_cdf(float x) {
+    return 0.5f * erfcf(-x * 0.70710678118654752440f);
+}
+__device__ __forceinline__ float gelu_f(float x) { return x * std_normal_cdf(x); }
+__device__ __forceinline__ float gelu_d(float x) {
+    return std_normal_cdf(x) + x * 0.39894228040143267794f * expf(-0.5f * x * x);
+}
+// kind: 0 = ReLU, 1 = GELU (the values of mp_act)
+template <int KIND>
+__device__ __forceinline__ uint16_t act_fwd1(uint16_t xh) {
+    if (KIND == 0) {
+        const float x = h2f(xh);
+        return (x > 0.0f || x != x) ? xh : uint16_t(0);
+    }
+    return f2h(gelu_f(h2f(xh)));
+}
+template <int KIND>
+__device__ __forceinline__ uint16_t act_bwd1(uint16_t xh, uint16_t dyh) {
+    const float x = h2f(xh);
+    if (KIND == 0) return x > 0.0f ? dyh : uint16_t(0);
+    return f2h(h2f(dyh) * gelu_d(x));
+}
+
 }  // namespace mp
