@@ -16,6 +16,7 @@ figures are reported beside it. `cpu_baseline` times the CPU oracle on a bounded
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,6 +33,21 @@ WIDTH, BATCH, LAYERS = 4096, 4096, 12
 SWEEP_BYTES_PER_PARAM = 20        # read g16 2 + w32 4 + v32 4, write w32 4 + v32 4 + w16 2
 CHECK_BYTES_PER_PARAM = 2
 
+# HBM-side bytes per launch from two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch) over `bench.py --pmc-kernel <kind>`, at the bench's shapes. FETCH_SIZE reads half
+# of the bytes a 1 GiB device copy moves and WRITE_SIZE all of them (`--pmc-kernel copy`), so the
+# fetch figure is scaled by 2.0 and the write figure by 1.0. A figure holds only for the kernel
+# source it was taken on: it is reported while the SHA-256 of those files still matches.
+MEASURED_TRAFFIC = {
+    "gemm": {"src": ["mp_gemm.hip", "mp_internal.h"],
+             "sha256": "f1e018cd65b9c224a50a8ca5da2c2ca583eb0199ceb1a62a7f46565d8791c0a5",
+             "fwd": (98648.5, 33124.9), "dgrad": (98650.8, 33127.4), "wgrad": (98776.9, 33129.6)},
+    "update": {"src": ["mp_step.hip", "mp_internal.h"],
+               "sha256": "faf1272f52adb76727778c41b5768651c3d17f51866f23b1fe6be103523f69b3",
+               "update": (988563.3, 1968544.7)},
+}
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -39,8 +55,54 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=12, help="batch rows of the oracle's sample step")
+    p.add_argument("--cpu-rows", type=int, default=32, help="batch rows of the oracle's sample step")
+    p.add_argument("--pmc-kernel", choices=["fwd", "dgrad", "wgrad", "update", "copy"],
+                   help="only launch this kernel --pmc-reps times at the bench's shape (for counter passes)")
+    p.add_argument("--pmc-reps", type=int, default=3)
     return p.parse_args()
+
+
+def source_sha256(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mixed_precision_neural_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(group: str, kind: str):
+    """Per-launch HBM bytes of the counter passes, or None once the kernel source has changed."""
+    t = MEASURED_TRAFFIC[group]
+    if source_sha256(t["src"]) != t["sha256"]:
+        return None
+    fetch_kib, write_kib = t[kind]
+    return round((fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024)
+
+
+def pmc_kernel(args, mp, torch):
+    """Launches one kernel kind a few times at the bench's shapes and nothing else of note."""
+    n = WIDTH
+    if args.pmc_kernel in ("fwd", "dgrad", "wgrad"):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        A = torch.randn(n, n, device="cuda", generator=g).half()
+        B = torch.randn(n, n, device="cuda", generator=g).half()
+        C = torch.empty(n, n, device="cuda", dtype=torch.float16)
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        f = {"fwd": lambda: mp.linear_fwd(A, B, Y=C), "dgrad": lambda: mp.linear_dgrad(A, B, dX=C),
+             "wgrad": lambda: mp.linear_wgrad(A, B, dW=C, found_inf=flag)}[args.pmc_kernel]
+    elif args.pmc_kernel == "update":
+        N = LAYERS * n * n
+        w = torch.randn(N, device="cuda"); v = torch.zeros(N, device="cuda")
+        gr = (torch.randn(N, device="cuda") * 1e-3).half(); h = torch.empty(N, device="cuda", dtype=torch.float16)
+        S = mp.Scaler(65536.0, True); pl = mp.ParamList([w], [v], [gr], [h])
+        f = lambda: mp.step(pl, S, 0.01, 0.9, 0.0, flags=mp.MP_GRADS_PRECHECKED)
+    else:                                   # calibration: 1 GiB read + 1 GiB written per launch
+        x = torch.randn(256 * 1024 * 1024, device="cuda"); y = torch.empty_like(x)
+        f = lambda: y.copy_(x)
+    for _ in range(args.pmc_reps):
+        f()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_kernel": args.pmc_kernel, "launches": args.pmc_reps}), flush=True)
 
 
 def calibration_c() -> float:
@@ -172,6 +234,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.pmc_kernel:
+        pmc_kernel(args, mp, torch)
+        return
     c = calibration_c()
     w = workloads.c4()
     model = Model(mp, torch, w, c)
@@ -236,13 +301,14 @@ def main():
                    "loss_multiplier_c": c},
         "roofline": {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": gemm[dom]["TFLOPs"],
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": gemm[dom]["frac"],
-                     "traffic": None},
+                     "traffic": measured_traffic("gemm", dom)},
         "gemm": gemm,
         "mp_step": {"bound": "hbm", "mode": "flag from the wgrad epilogues, one update pass",
                     "avg_us": round(sweep_ms * 1e3, 2),
                     "achieved_GBps": round(sweep_gbps, 1), "peak": PEAK_HBM_GBPS,
                     "frac": round(sweep_gbps / PEAK_HBM_GBPS, 4),
                     "algorithmic_bytes": SWEEP_BYTES_PER_PARAM * nparam,
+                    "traffic": measured_traffic("update", "update"),
                     "two_pass_us": round(two_pass_ms * 1e3, 2),
                     "two_pass_GBps": round(SWEEP_BYTES_PER_PARAM * nparam / (two_pass_ms * 1e-3) / 1e9, 1),
                     "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam},
