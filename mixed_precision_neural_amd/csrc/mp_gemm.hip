@@ -57,6 +57,7 @@ struct GemmArgs {
     int64_t Mc, Nc, R;           // output rows, output columns, reduction length
     uint32_t* flag;              // nullable: OR 1 if any binary16 output is inf/NaN
     int a_vec, b_vec;            // 16-byte global loads allowed for A / B
+    int c_vec;                   // 16-byte output stores allowed (aligned base, ldc % 8 == 0 / % 4 for FP32)
     int tiles_m, tiles_n;
 };
 
@@ -206,7 +207,7 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
         }
     };
 
@@ -298,29 +299,83 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
         reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, false, FM, FN>(g, lds, row0, col0, tid, lane,
                                                                        wm, wn, acc);
 
-    // ---- epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
+    // ---- epilogue. The MFMA takes B's fragment as its first operand, so the
+    // accumulator of block (i, j) holds the transposed tile: lane l has output
+    // row m = 32 i + (l & 31) and, in register r, column n = 32 j + 8 (r / 4) +
+    // 4 (l / 32) + r % 4 (wave-local), i.e. four consecutive columns of one row
+    // per group of four registers.
+    const int64_t wrow0 = row0 + wm * WTM, wcol0 = col0 + wn * WTN;
+    if (EPI == kEpiF32) {
+        float* C = static_cast<float*>(g.C);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t gr = wrow0 + i * 32 + (lane & 31);
+                    const int64_t gc = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
+                    if (gr >= g.Mc) continue;
+                    float* dst = C + gr * g.ldc + gc;
+                    if (g.c_vec && gc + 4 <= g.Nc) {
+                        *reinterpret_cast<mp::f32x4*>(dst) =
+                            mp::f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (gc + e < g.Nc) dst[e] = acc[i][j][4 * q + e];
+                    }
+                }
+        return;
+    }
+    // Binary16 out, staged through LDS (free once the reduction has ended): each
+    // wave rounds its WTM x WTN tile, writes it row-major into its own LDS region
+    // with 8-byte stores (16-byte chunk c of row m at chunk c ^ (m mod chunks)),
+    // then reads it back a 16-byte row piece per lane and stores whole rows.
+    constexpr int kChunks = WTN / 8;                     // 16-byte chunks per staged row
+    constexpr int kRowsPerPass = 64 / kChunks;
+    static_assert(WTM * WTN * 2 * WAVES_M * WAVES_N <= 2 * kStage * 16, "staged tile must fit in LDS");
+    static_assert(WTM % kRowsPerPass == 0, "whole passes");
     uint32_t bad = 0;
+    uint8_t* stage = reinterpret_cast<uint8_t*>(lds) + size_t(wave) * WTM * WTN * 2;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t gc = col0 + wn * WTN + j * 32 + (lane & 31);
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t gr =
-                    row0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (gr < g.Mc && gc < g.Nc) {
-                    if (EPI == kEpiF32) {
-                        static_cast<float*>(g.C)[gr * g.ldc + gc] = acc[i][j][r];
-                    } else {
-                        const uint16_t h = mp::f2h(acc[i][j][r]);
-                        bad |= mp::nonfinite1(h);
-                        static_cast<uint16_t*>(g.C)[gr * g.ldc + gc] = h;
-                    }
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int m = i * 32 + (lane & 31);
+                const int c = (j * 32 + 8 * q) / 8;            // chunk of the 8 columns 32 j + 8 q ..
+                const uint32_t h0 = mp::f2h(acc[i][j][4 * q]), h1 = mp::f2h(acc[i][j][4 * q + 1]);
+                const uint32_t h2 = mp::f2h(acc[i][j][4 * q + 2]), h3 = mp::f2h(acc[i][j][4 * q + 3]);
+                const uint2 v = make_uint2(h0 | h1 << 16, h2 | h3 << 16);
+                *reinterpret_cast<uint2*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16 +
+                                          8 * (lane >> 5)) = v;
             }
+    __syncthreads();
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+#pragma unroll 4
+    for (int p = 0; p < WTM / kRowsPerPass; ++p) {
+        const int m = p * kRowsPerPass + lane / kChunks, c = lane % kChunks;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16);
+        const int64_t gr = wrow0 + m, gc = wcol0 + 8 * c;
+        if (gr >= g.Mc) continue;
+        uint16_t* dst = C + gr * g.ldc + gc;
+        if (g.c_vec && gc + 8 <= g.Nc) {
+            *reinterpret_cast<uint4*>(dst) = v;
+            bad |= mp::nonfinite2(v.x) | mp::nonfinite2(v.y) | mp::nonfinite2(v.z) | mp::nonfinite2(v.w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gc + e < g.Nc) {
+                    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+                    const uint16_t h = uint16_t(w >> (16 * (e & 1)));
+                    dst[e] = h;
+                    bad |= mp::nonfinite1(h);
+                }
         }
-    if (EPI == kEpiF16 && g.flag) {
+    }
+    if (g.flag) {
         if (__syncthreads_or(bad) && tid == 0) atomicOr(g.flag, 1u);
     }
 }
@@ -351,6 +406,10 @@ bool bad_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld) {
 
 // 16-byte loads need a 16-byte aligned base and a row pitch of 8 elements.
 int vec_ok(const void* p, int64_t ld) { return mp::aligned16(p) && (ld % 8) == 0; }
+// 16-byte output stores: 8 binary16 or 4 FP32 values per row piece.
+int out_vec_ok(const void* p, int64_t ld, mp_dtype t) {
+    return mp::aligned16(p) && (ld % (t == MP_F16 ? 8 : 4)) == 0;
+}
 
 bool too_large(int64_t Mc, int64_t Nc) {
     // tile counts must fit a 32-bit grid
@@ -368,7 +427,8 @@ extern "C" mp_status mp_linear_fwd(const uint16_t* X, int64_t ldx, const uint16_
     if (bad_matrix(X, M, K, ldx) || bad_matrix(W, N, K, ldw) || bad_matrix(Y, M, N, ldy))
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(M, N)) return MP_ERR_INVALID_ARGUMENT;
-    GemmArgs a{X, W, Y, ldx, ldw, ldy, M, N, K, nullptr, vec_ok(X, ldx), vec_ok(W, ldw), 0, 0};
+    GemmArgs a{X, W, Y, ldx, ldw, ldy, M, N, K, nullptr, vec_ok(X, ldx), vec_ok(W, ldw),
+               out_vec_ok(Y, ldy, y_dtype), 0, 0};
     hipStream_t s = mp::as_stream(stream);
     if (y_dtype == MP_F16) return launch<true, true, kEpiF16>(a, s, "mp_linear_fwd");
     return launch<true, true, kEpiF32>(a, s, "mp_linear_fwd");
@@ -383,7 +443,8 @@ extern "C" mp_status mp_linear_dgrad(const uint16_t* dY, int64_t lddy, const uin
     if (bad_matrix(dY, M, N, lddy) || bad_matrix(W, N, K, ldw) || bad_matrix(dX, M, K, lddx))
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(M, K)) return MP_ERR_INVALID_ARGUMENT;
-    GemmArgs a{dY, W, dX, lddy, ldw, lddx, M, K, N, nullptr, vec_ok(dY, lddy), vec_ok(W, ldw), 0, 0};
+    GemmArgs a{dY, W, dX, lddy, ldw, lddx, M, K, N, nullptr, vec_ok(dY, lddy), vec_ok(W, ldw),
+               out_vec_ok(dX, lddx, dx_dtype), 0, 0};
     hipStream_t s = mp::as_stream(stream);
     if (dx_dtype == MP_F16) return launch<true, false, kEpiF16>(a, s, "mp_linear_dgrad");
     return launch<true, false, kEpiF32>(a, s, "mp_linear_dgrad");
@@ -400,7 +461,8 @@ extern "C" mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uin
     if (bad_matrix(dY, M, N, lddy) || bad_matrix(X, M, K, ldx) || bad_matrix(dW, N, K, lddw))
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(N, K)) return MP_ERR_INVALID_ARGUMENT;
-    GemmArgs a{dY, X, dW, lddy, ldx, lddw, N, K, M, found_inf, vec_ok(dY, lddy), vec_ok(X, ldx), 0, 0};
+    GemmArgs a{dY, X, dW, lddy, ldx, lddw, N, K, M, found_inf, vec_ok(dY, lddy), vec_ok(X, ldx),
+               out_vec_ok(dW, lddw, dw_dtype), 0, 0};
     hipStream_t s = mp::as_stream(stream);
     if (dw_dtype == MP_F16) return launch<false, false, kEpiF16>(a, s, "mp_linear_wgrad");
     return launch<false, false, kEpiF32>(a, s, "mp_linear_wgrad");
