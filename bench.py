@@ -56,7 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=32, help="batch rows of the oracle's sample step")
-    p.add_argument("--pmc-kernel", choices=["fwd", "dgrad", "wgrad", "update", "copy"],
+    p.add_argument("--unfused", action="store_true",
+                   help="GELU as separate point-wise kernels instead of in the GEMM epilogues")
+    p.add_argument("--pmc-kernel", choices=["fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad", "update", "copy"],
                    help="only launch this kernel --pmc-reps times at the bench's shape (for counter passes)")
     p.add_argument("--pmc-reps", type=int, default=3)
     return p.parse_args()
@@ -73,7 +75,7 @@ def source_sha256(files) -> str:
 def measured_traffic(group: str, kind: str):
     """Per-launch HBM bytes of the counter passes, or None once the kernel source has changed."""
     t = MEASURED_TRAFFIC[group]
-    if source_sha256(t["src"]) != t["sha256"]:
+    if source_sha256(t["src"]) != t["sha256"] or kind not in t:
         return None
     fetch_kib, write_kib = t[kind]
     return round((fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024)
@@ -82,13 +84,17 @@ def measured_traffic(group: str, kind: str):
 def pmc_kernel(args, mp, torch):
     """Launches one kernel kind a few times at the bench's shapes and nothing else of note."""
     n = WIDTH
-    if args.pmc_kernel in ("fwd", "dgrad", "wgrad"):
+    if args.pmc_kernel in ("fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad"):
         g = torch.Generator(device="cuda").manual_seed(0)
         A = torch.randn(n, n, device="cuda", generator=g).half()
         B = torch.randn(n, n, device="cuda", generator=g).half()
         C = torch.empty(n, n, device="cuda", dtype=torch.float16)
+        D = torch.randn(n, n, device="cuda", generator=g).half()
         flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-        f = {"fwd": lambda: mp.linear_fwd(A, B, Y=C), "dgrad": lambda: mp.linear_dgrad(A, B, dX=C),
+        f = {"fwd": lambda: mp.linear_fwd(A, B, Y=C),
+             "fwd_act": lambda: mp.linear_fwd_act(mp.GELU, A, B, Z=C, H=D),
+             "dgrad": lambda: mp.linear_dgrad(A, B, dX=C),
+             "dgrad_act": lambda: mp.linear_dgrad_act(mp.GELU, A, B, D, dZ=C),
              "wgrad": lambda: mp.linear_wgrad(A, B, dW=C, found_inf=flag)}[args.pmc_kernel]
     elif args.pmc_kernel == "update":
         N = LAYERS * n * n
@@ -128,11 +134,13 @@ class Model:
         self.H = [torch.empty((BATCH, WIDTH), dtype=f16, device=dev) for _ in range(LAYERS - 1)]
         self.dA = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)
         self.dB = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)
+        self.dC = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)   # unfused variant only
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self.scaler = mp.Scaler(w.scale, w.dynamic, w.growth_interval)
         self.plist = mp.ParamList(self.W, self.V, self.G, self.W16)
         self.hp = (w.lr, w.momentum, w.weight_decay)
         self.events = None
+        self.fused = True
 
     def _t(self, kind, fn, *a, **k):
         if self.events is None:
@@ -149,19 +157,29 @@ class Model:
         mp, t = self.mp, self._t
         inp = self.X
         for l in range(LAYERS):
-            t("fwd", mp.linear_fwd, inp, self.W16[l], Y=self.Z[l])
-            if l < LAYERS - 1:
+            if l == LAYERS - 1:
+                t("fwd", mp.linear_fwd, inp, self.W16[l], Y=self.Z[l])
+            elif self.fused:
+                t("fwd_act", mp.linear_fwd_act, mp.GELU, inp, self.W16[l], Z=self.Z[l], H=self.H[l])
+                inp = self.H[l]
+            else:
+                t("fwd", mp.linear_fwd, inp, self.W16[l], Y=self.Z[l])
                 t("gelu_fwd", mp.act_fwd, mp.GELU, self.Z[l], self.H[l])
                 inp = self.H[l]
         t("loss", mp.loss_mse, self.Z[-1], self.T, self.c, self.scaler, self.loss, self.dA)
-        dZ, dH = self.dA, self.dB
+        dZ, other = self.dA, self.dB
         for l in range(LAYERS - 1, -1, -1):
-            if l < LAYERS - 1:
-                t("gelu_bwd", mp.act_bwd, mp.GELU, self.Z[l], dH, dZ)
             prev = self.X if l == 0 else self.H[l - 1]
             t("wgrad", mp.linear_wgrad, dZ, prev, dW=self.G[l], found_inf=self.scaler.found_inf_ptr)
-            if l > 0:
-                t("dgrad", mp.linear_dgrad, dZ, self.W16[l], dX=dH)
+            if l == 0:
+                break
+            if self.fused:
+                # dZ_{l-1} = GELU'(Z_{l-1}) * (dZ_l . W_l) in the dgrad epilogue
+                t("dgrad_act", mp.linear_dgrad_act, mp.GELU, dZ, self.W16[l], self.Z[l - 1], dZ=other)
+            else:
+                t("dgrad", mp.linear_dgrad, dZ, self.W16[l], dX=self.dC)
+                t("gelu_bwd", mp.act_bwd, mp.GELU, self.Z[l - 1], self.dC, other)
+            dZ, other = other, dZ
         lr, mu, wd = self.hp
         # the weight-gradient epilogues already set the overflow flag (Step 6
         # fused into the producer), so the sweep is the single update pass
@@ -240,6 +258,7 @@ def main():
     c = calibration_c()
     w = workloads.c4()
     model = Model(mp, torch, w, c)
+    model.fused = not args.unfused
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -273,11 +292,12 @@ def main():
     step_flop = gemm_flop * (3 * LAYERS - 1)
     value = step_flop / (ms * 1e-3) / 1e12
     gemm = {}
-    for k in ("fwd", "dgrad", "wgrad"):
+    kinds = [k for k in ("fwd_act", "fwd", "dgrad_act", "dgrad", "wgrad") if k in kern]
+    for k in kinds:
         tf = gemm_flop / (kern[k]["avg_ms"] * 1e-3) / 1e12
         gemm[k] = {"avg_us": round(kern[k]["avg_ms"] * 1e3, 2), "TFLOPs": round(tf, 1),
                    "frac": round(tf / PEAK_F16_TFLOPS, 4), "launches": kern[k]["launches"]}
-    dom = max(("fwd", "dgrad", "wgrad"), key=lambda k: kern[k]["total_ms"])
+    dom = max(kinds, key=lambda k: kern[k]["total_ms"])
     nparam = LAYERS * WIDTH * WIDTH
     sweep_ms = kern["sweep"]["avg_ms"]
     sweep_gbps = SWEEP_BYTES_PER_PARAM * nparam / (sweep_ms * 1e-3) / 1e9
@@ -298,6 +318,7 @@ def main():
                                "FP16 storage, FP32 master + momentum, dynamic loss scale 2^16, "
                                "SGD lr 0.01 momentum 0.9",
                    "global_batch": BATCH, "params": nparam, "gemms_per_step": 3 * LAYERS - 1,
+                   "gelu": "separate point-wise kernels" if args.unfused else "in the GEMM epilogues",
                    "loss_multiplier_c": c},
         "roofline": {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": gemm[dom]["TFLOPs"],
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": gemm[dom]["frac"],
@@ -312,7 +333,8 @@ def main():
                     "two_pass_us": round(two_pass_ms * 1e3, 2),
                     "two_pass_GBps": round(SWEEP_BYTES_PER_PARAM * nparam / (two_pass_ms * 1e-3) / 1e9, 1),
                     "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam},
-        "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")},
+        "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")
+                   if k in kern},
         "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},
         "wall_s": round(wall, 3),
     }

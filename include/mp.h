@@ -99,6 +99,9 @@ typedef void* mp_stream;
  * the rounding error of FP32 accumulation.
  * ------------------------------------------------------------------------ */
 
+/* Point-wise activation of the fused epilogues and of mp_act_fwd/bwd. */
+typedef enum { MP_ACT_RELU = 0, MP_ACT_GELU = 1 } mp_act;
+
 /* Forward: Y[M, N] = X[M, K] . W[N, K]^T.
  * X: ldx >= K; W: ldw >= K; Y: ldy >= N, element type y_dtype.
  * Errors: MP_ERR_INVALID_ARGUMENT for negative sizes, a leading dimension
@@ -124,6 +127,32 @@ mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uint16_t* X, i
                           void* dW, int64_t lddw, mp_dtype dw_dtype,
                           int64_t M, int64_t N, int64_t K, uint32_t* found_inf,
                           mp_stream stream);
+
+/* Forward of an activated layer in one pass: Z[M, N] = RNE16(X . W^T) as in
+ * mp_linear_fwd with a binary16 output, and H = act(Z) elementwise, both
+ * stored. The bits of Z and H equal those of mp_linear_fwd followed by
+ * mp_act_fwd; the activation is applied while the output tile is written,
+ * so Z is not read back from memory. Source: the analysis page, §3.4 "The
+ * Integrated Training Procedure", Step 2 (the forward pass, whose point-wise
+ * operations are memory-bound and may run in binary16 or FP32).
+ * X: ldx >= K; W: ldw >= K; Z: ldz >= N; H: ldh >= N. Z and H must not
+ * overlap each other or the inputs.
+ * Errors: MP_ERR_INVALID_ARGUMENT for an unknown kind and as mp_linear_fwd. */
+mp_status mp_linear_fwd_act(mp_act kind, const uint16_t* X, int64_t ldx, const uint16_t* W,
+                            int64_t ldw, uint16_t* Z, int64_t ldz, uint16_t* H, int64_t ldh,
+                            int64_t M, int64_t N, int64_t K, mp_stream stream);
+
+/* Activation gradient through an activated layer in one pass:
+ * dZ[M, K] = RNE16(act'(Z) * RNE16(dY . W)), i.e. the bits of mp_linear_dgrad
+ * (binary16 output) followed by mp_act_bwd with the saved pre-activation Z,
+ * without storing the intermediate. Stays multiplied by the loss scale.
+ * Source: the analysis page, §3.4 "The Integrated Training Procedure",
+ * Step 4. dY: lddy >= N; W: ldw >= K; Z: ldz >= K; dZ: lddz >= K. dZ must
+ * not overlap the inputs.
+ * Errors: MP_ERR_INVALID_ARGUMENT for an unknown kind and as mp_linear_dgrad. */
+mp_status mp_linear_dgrad_act(mp_act kind, const uint16_t* dY, int64_t lddy, const uint16_t* W,
+                              int64_t ldw, const uint16_t* Z, int64_t ldz, uint16_t* dZ,
+                              int64_t lddz, int64_t M, int64_t N, int64_t K, mp_stream stream);
 
 /* ------------------------------------------------------------------------
  * The optimizer sweep over a ragged list of parameter tensors.
@@ -207,7 +236,6 @@ mp_status mp_scaler_update(mp_scaler* scaler, mp_stream stream);
 /* w16[i] = round-to-nearest-even binary16 of w32[i] (Step 1 at init). */
 mp_status mp_round_f32_to_f16(const float* w32, uint16_t* w16, int64_t n, mp_stream stream);
 
-typedef enum { MP_ACT_RELU = 0, MP_ACT_GELU = 1 } mp_act;
 
 /* y = act(x), elementwise over n binary16 values. GELU is x * Phi(x) with
  * the exact error function. */

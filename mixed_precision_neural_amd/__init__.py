@@ -64,6 +64,8 @@ def lib() -> C.CDLL:
         L.mp_linear_fwd.argtypes = [vp, i64, vp, i64, vp, i64, C.c_int, i64, i64, i64, vp]
         L.mp_linear_dgrad.argtypes = [vp, i64, vp, i64, vp, i64, C.c_int, i64, i64, i64, vp]
         L.mp_linear_wgrad.argtypes = [vp, i64, vp, i64, vp, i64, C.c_int, i64, i64, i64, vp, vp]
+        L.mp_linear_fwd_act.argtypes = [C.c_int, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+        L.mp_linear_dgrad_act.argtypes = [C.c_int, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
         L.mp_param_list_create.argtypes = [vp, i32, C.POINTER(vp), vp]
         L.mp_param_list_destroy.argtypes = [vp]
         L.mp_param_list_numel.argtypes = [vp]
@@ -157,6 +159,37 @@ def linear_dgrad(dY: torch.Tensor, W: torch.Tensor, dX: torch.Tensor | None = No
     _check(lib().mp_linear_dgrad(pd, ldd, pw, ldw, px, ldx, dt, M, N, K, _stream(stream)),
            "mp_linear_dgrad")
     return dX
+
+
+def linear_fwd_act(kind: int, X: torch.Tensor, W: torch.Tensor, Z: torch.Tensor | None = None,
+                   H: torch.Tensor | None = None, stream=None):
+    """Z = RNE16(X . W^T) and H = act(Z) in one kernel; returns (Z, H)."""
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    Z = _out(Z, (M, N), torch.float16, X.device)
+    H = _out(H, (M, N), torch.float16, X.device)
+    px, ldx = _mat(X, "X"); pw, ldw = _mat(W, "W"); pz, ldz = _mat(Z, "Z"); ph, ldh = _mat(H, "H")
+    _check(lib().mp_linear_fwd_act(int(kind), px, ldx, pw, ldw, pz, ldz, ph, ldh, M, N, K, _stream(stream)),
+           "mp_linear_fwd_act")
+    return Z, H
+
+
+def linear_dgrad_act(kind: int, dY: torch.Tensor, W: torch.Tensor, Z: torch.Tensor,
+                     dZ: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """dZ = RNE16(act'(Z) * RNE16(dY . W)) in one kernel."""
+    M, N = dY.shape
+    K = W.shape[1]
+    if W.shape[0] != N:
+        raise ValueError("W must be [N, K]")
+    if tuple(Z.shape) != (M, K):
+        raise ValueError("Z must be [M, K]")
+    dZ = _out(dZ, (M, K), torch.float16, dY.device)
+    pd, ldd = _mat(dY, "dY"); pw, ldw = _mat(W, "W"); pz, ldz = _mat(Z, "Z"); po, ldo = _mat(dZ, "dZ")
+    _check(lib().mp_linear_dgrad_act(int(kind), pd, ldd, pw, ldw, pz, ldz, po, ldo, M, N, K, _stream(stream)),
+           "mp_linear_dgrad_act")
+    return dZ
 
 
 def linear_wgrad(dY: torch.Tensor, X: torch.Tensor, dW: torch.Tensor | None = None,

@@ -58,12 +58,18 @@ struct GemmArgs {
     uint32_t* flag;              // nullable: OR 1 if any binary16 output is inf/NaN
     int a_vec, b_vec;            // 16-byte global loads allowed for A / B
     int c_vec;                   // 16-byte output stores allowed (aligned base, ldc % 8 == 0 / % 4 for FP32)
+    void* C2;                    // kEpiAct: act(C) (binary16), ldc2
+    const uint16_t* Z;           // kEpiDact: saved pre-activation (binary16), ldz
+    int64_t ldc2, ldz;
+    int aux_vec;                 // 16-byte access allowed for C2 / Z
     int tiles_m, tiles_n;
 };
 
 // Epilogue modes.
 constexpr int kEpiF32 = 0;       // C = acc (FP32)
 constexpr int kEpiF16 = 1;       // C = RNE16(acc)
+constexpr int kEpiAct = 2;       // C = RNE16(acc), C2 = act(C)             (forward of an activated layer)
+constexpr int kEpiDact = 3;      // C = act'(Z) * RNE16(acc), rounded once  (dgrad into an activated layer)
 
 __device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
 template <int CHUNKS>
@@ -257,7 +263,21 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int EPI>
+// Applies the binary16 point-wise tail of the epilogue to one output element
+// h = RNE16(acc) and stores it (z: the saved pre-activation, kEpiDact only).
+template <int EPI, int KIND>
+__device__ __forceinline__ uint16_t epi_main(uint16_t h, uint16_t z) {
+    if (EPI == kEpiDact) return mp::act_bwd1<KIND>(z, h);
+    return h;
+}
+__device__ __forceinline__ uint16_t half_of(const uint4& v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return uint16_t(w >> (16 * (e & 1)));
+}
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return uint32_t(lo) | uint32_t(hi) << 16; }
+
+// KIND (the activation of kEpiAct / kEpiDact, an mp_act value) is ignored by the other modes.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int EPI, int KIND>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArgs g) {
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -361,41 +381,63 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
         const int64_t gr = wrow0 + m, gc = wcol0 + 8 * c;
         if (gr >= g.Mc) continue;
         uint16_t* dst = C + gr * g.ldc + gc;
-        if (g.c_vec && gc + 8 <= g.Nc) {
-            *reinterpret_cast<uint4*>(dst) = v;
-            bad |= mp::nonfinite2(v.x) | mp::nonfinite2(v.y) | mp::nonfinite2(v.z) | mp::nonfinite2(v.w);
+        if (g.c_vec && gc + 8 <= g.Nc && (EPI == kEpiF16 || g.aux_vec)) {
+            if (EPI == kEpiF16) {
+                *reinterpret_cast<uint4*>(dst) = v;
+                bad |= mp::nonfinite2(v.x) | mp::nonfinite2(v.y) | mp::nonfinite2(v.z) | mp::nonfinite2(v.w);
+            } else if (EPI == kEpiAct) {
+                *reinterpret_cast<uint4*>(dst) = v;
+                uint16_t a[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = mp::act_fwd1<KIND>(half_of(v, e));
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
+                    make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+            } else {
+                const uint4 z = *reinterpret_cast<const uint4*>(g.Z + gr * g.ldz + gc);
+                uint16_t d[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d[e] = epi_main<EPI, KIND>(half_of(v, e), half_of(z, e));
+                *reinterpret_cast<uint4*>(dst) =
+                    make_uint4(pack2(d[0], d[1]), pack2(d[2], d[3]), pack2(d[4], d[5]), pack2(d[6], d[7]));
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (gc + e < g.Nc) {
-                    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-                    const uint16_t h = uint16_t(w >> (16 * (e & 1)));
-                    dst[e] = h;
-                    bad |= mp::nonfinite1(h);
+                    const uint16_t h = half_of(v, e);
+                    if (EPI == kEpiF16) {
+                        dst[e] = h;
+                        bad |= mp::nonfinite1(h);
+                    } else if (EPI == kEpiAct) {
+                        dst[e] = h;
+                        static_cast<uint16_t*>(g.C2)[gr * g.ldc2 + gc + e] = mp::act_fwd1<KIND>(h);
+                    } else {
+                        dst[e] = epi_main<EPI, KIND>(h, g.Z[gr * g.ldz + gc + e]);
+                    }
                 }
         }
     }
-    if (g.flag) {
+    if (EPI == kEpiF16 && g.flag) {
         if (__syncthreads_or(bad) && tid == 0) atomicOr(g.flag, 1u);
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool A_KC, bool B_KC, int EPI>
+template <int BM, int BN, int WM, int WN, bool A_KC, bool B_KC, int EPI, int KIND>
 mp_status launch_cfg(GemmArgs a, hipStream_t s, const char* name) {
     a.tiles_m = int((a.Mc + BM - 1) / BM);
     a.tiles_n = int((a.Nc + BN - 1) / BN);
     const uint32_t blocks = uint32_t(a.tiles_m) * uint32_t(a.tiles_n);
-    gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, EPI><<<blocks, 64 * WM * WN, 0, s>>>(a);
+    gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, EPI, KIND><<<blocks, 64 * WM * WN, 0, s>>>(a);
     return mp::launch_status(name);
 }
 
-template <bool A_KC, bool B_KC, int EPI>
+template <bool A_KC, bool B_KC, int EPI, int KIND = 0>
 mp_status launch(GemmArgs a, hipStream_t s, const char* name) {
     // Large outputs: 256 x 256 tiles, 4 waves of 128 x 128. Small outputs
     // (where a 256 x 256 grid would leave most of the 256 CUs idle): 64 x 64.
     const int64_t big_tiles = ((a.Mc + 255) / 256) * ((a.Nc + 255) / 256);
-    if (big_tiles >= 128) return launch_cfg<256, 256, 2, 2, A_KC, B_KC, EPI>(a, s, name);
-    return launch_cfg<64, 64, 2, 2, A_KC, B_KC, EPI>(a, s, name);
+    if (big_tiles >= 128) return launch_cfg<256, 256, 2, 2, A_KC, B_KC, EPI, KIND>(a, s, name);
+    return launch_cfg<64, 64, 2, 2, A_KC, B_KC, EPI, KIND>(a, s, name);
 }
 
 bool bad_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld) {
@@ -428,7 +470,7 @@ extern "C" mp_status mp_linear_fwd(const uint16_t* X, int64_t ldx, const uint16_
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(M, N)) return MP_ERR_INVALID_ARGUMENT;
     GemmArgs a{X, W, Y, ldx, ldw, ldy, M, N, K, nullptr, vec_ok(X, ldx), vec_ok(W, ldw),
-               out_vec_ok(Y, ldy, y_dtype), 0, 0};
+               out_vec_ok(Y, ldy, y_dtype)};
     hipStream_t s = mp::as_stream(stream);
     if (y_dtype == MP_F16) return launch<true, true, kEpiF16>(a, s, "mp_linear_fwd");
     return launch<true, true, kEpiF32>(a, s, "mp_linear_fwd");
@@ -444,7 +486,7 @@ extern "C" mp_status mp_linear_dgrad(const uint16_t* dY, int64_t lddy, const uin
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(M, K)) return MP_ERR_INVALID_ARGUMENT;
     GemmArgs a{dY, W, dX, lddy, ldw, lddx, M, K, N, nullptr, vec_ok(dY, lddy), vec_ok(W, ldw),
-               out_vec_ok(dX, lddx, dx_dtype), 0, 0};
+               out_vec_ok(dX, lddx, dx_dtype)};
     hipStream_t s = mp::as_stream(stream);
     if (dx_dtype == MP_F16) return launch<true, false, kEpiF16>(a, s, "mp_linear_dgrad");
     return launch<true, false, kEpiF32>(a, s, "mp_linear_dgrad");
@@ -462,8 +504,42 @@ extern "C" mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uin
         return MP_ERR_INVALID_ARGUMENT;
     if (too_large(N, K)) return MP_ERR_INVALID_ARGUMENT;
     GemmArgs a{dY, X, dW, lddy, ldx, lddw, N, K, M, found_inf, vec_ok(dY, lddy), vec_ok(X, ldx),
-               out_vec_ok(dW, lddw, dw_dtype), 0, 0};
+               out_vec_ok(dW, lddw, dw_dtype)};
     hipStream_t s = mp::as_stream(stream);
     if (dw_dtype == MP_F16) return launch<false, false, kEpiF16>(a, s, "mp_linear_wgrad");
     return launch<false, false, kEpiF32>(a, s, "mp_linear_wgrad");
+}
+
+extern "C" mp_status mp_linear_fwd_act(mp_act kind, const uint16_t* X, int64_t ldx, const uint16_t* W,
+                                       int64_t ldw, uint16_t* Z, int64_t ldz, uint16_t* H, int64_t ldh,
+                                       int64_t M, int64_t N, int64_t K, mp_stream stream) {
+    if (kind != MP_ACT_RELU && kind != MP_ACT_GELU) return MP_ERR_INVALID_ARGUMENT;
+    if (M < 0 || N < 0 || K < 0) return MP_ERR_INVALID_ARGUMENT;
+    if (M == 0 || N == 0) return MP_OK;
+    if (bad_matrix(X, M, K, ldx) || bad_matrix(W, N, K, ldw) || bad_matrix(Z, M, N, ldz) ||
+        bad_matrix(H, M, N, ldh))
+        return MP_ERR_INVALID_ARGUMENT;
+    if (too_large(M, N)) return MP_ERR_INVALID_ARGUMENT;
+    GemmArgs a{X, W, Z, ldx, ldw, ldz, M, N, K, nullptr, vec_ok(X, ldx), vec_ok(W, ldw),
+               out_vec_ok(Z, ldz, MP_F16), H, nullptr, ldh, 0, out_vec_ok(H, ldh, MP_F16)};
+    hipStream_t s = mp::as_stream(stream);
+    if (kind == MP_ACT_RELU) return launch<true, true, kEpiAct, MP_ACT_RELU>(a, s, "mp_linear_fwd_act");
+    return launch<true, true, kEpiAct, MP_ACT_GELU>(a, s, "mp_linear_fwd_act");
+}
+
+extern "C" mp_status mp_linear_dgrad_act(mp_act kind, const uint16_t* dY, int64_t lddy, const uint16_t* W,
+                                         int64_t ldw, const uint16_t* Z, int64_t ldz, uint16_t* dZ,
+                                         int64_t lddz, int64_t M, int64_t N, int64_t K, mp_stream stream) {
+    if (kind != MP_ACT_RELU && kind != MP_ACT_GELU) return MP_ERR_INVALID_ARGUMENT;
+    if (M < 0 || N < 0 || K < 0) return MP_ERR_INVALID_ARGUMENT;
+    if (M == 0 || K == 0) return MP_OK;
+    if (bad_matrix(dY, M, N, lddy) || bad_matrix(W, N, K, ldw) || bad_matrix(Z, M, K, ldz) ||
+        bad_matrix(dZ, M, K, lddz))
+        return MP_ERR_INVALID_ARGUMENT;
+    if (too_large(M, K)) return MP_ERR_INVALID_ARGUMENT;
+    GemmArgs a{dY, W, dZ, lddy, ldw, lddz, M, K, N, nullptr, vec_ok(dY, lddy), vec_ok(W, ldw),
+               out_vec_ok(dZ, lddz, MP_F16), nullptr, Z, 0, ldz, vec_ok(Z, ldz)};
+    hipStream_t s = mp::as_stream(stream);
+    if (kind == MP_ACT_RELU) return launch<true, false, kEpiDact, MP_ACT_RELU>(a, s, "mp_linear_dgrad_act");
+    return launch<true, false, kEpiDact, MP_ACT_GELU>(a, s, "mp_linear_dgrad_act");
 }

@@ -40,7 +40,15 @@ __device__ __forceinline__ float h2f(uint16_t h) {
     _Float16 x = __builtin_bit_cast(_Float16, h);
     return static_cast<float>(x);
 }
+// The FP32 value is pinned in a register first (an empty asm the optimiser
+// cannot see through), so the conversion is never merged with the operation
+// that produced the value: a mixed-precision v_fma_mix*_f16 would round the
+// exact product once, where every caller means "round to FP32, then to
+// binary16". Without the pin the compiler picks either form depending on the
+// surrounding code, and two kernels evaluating the same expression can differ
+// in the last bit when the FP32 result is a binary16 tie.
 __device__ __forceinline__ uint16_t f2h(float f) {
+    asm("" : "+v"(f));
     _Float16 x = static_cast<_Float16>(f);
     return __builtin_bit_cast(uint16_t, x);
 }

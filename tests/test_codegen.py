@@ -1,0 +1,67 @@
+"""Instruction-level guarantees of the gfx950 build, checked on the generated assembly.
+
+The update follows "Mixed Precision Training", long-form analysis page, §3.4 "The
+Integrated Training Procedure", Step 7: each FP32 operation rounds on its own, so the
+update kernel must contain no fused multiply-add of any kind. Every FP32 -> binary16
+rounding is meant as "round the FP32 value": a mixed-precision v_fma_mix*_f16 (which
+rounds the exact product once) must not appear in any kernel, or two kernels computing
+the same expression can differ in the last bit on binary16 ties.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixed_precision_neural_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def build_flags():
+    """The library's own compile flags (build.py loaded by path: no package import)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_mp_build", os.path.join(ROOT, "mixed_precision_neural_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.FLAGS
+
+
+def device_asm(name, tmp_path):
+    out = tmp_path / (name + ".s")
+    cmd = [HIPCC, *build_flags(), "--cuda-device-only", "-S",
+           os.path.join(CSRC, name + ".hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernel_bodies(asm):
+    """{symbol: text} for every kernel entry in the assembly."""
+    bodies, name, cur = {}, None, []
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name, cur = m.group(1), []
+            bodies[name] = cur
+        elif name is not None:
+            cur.append(line)
+            if "s_endpgm" in line:
+                name = None
+    return {k: "\n".join(v) for k, v in bodies.items()}
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+@pytest.mark.parametrize("name", ["mp_step", "mp_aux", "mp_gemm"])
+def test_no_mixed_precision_fma(name, tmp_path):
+    asm = device_asm(name, tmp_path)
+    assert "v_fma_mix" not in asm and "v_mad_mix" not in asm
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_update_kernel_has_no_fused_multiply_add(tmp_path):
+    bodies = kernel_bodies(device_asm("mp_step", tmp_path))
+    upd = [v for k, v in bodies.items() if "update_kernel" in k]
+    assert upd, "update kernel not found in the assembly"
+    for body in upd:
+        assert not re.search(r"\bv_(fma|fmac|mad|mac|pk_fma|pk_mul|pk_add)\w*", body)

@@ -1,0 +1,133 @@
+"""GPU parity of the activation-fused dot-product layers.
+
+Source: "Mixed Precision Training", long-form analysis page, §3.4 "The Integrated
+Training Procedure", Steps 2 and 4: a layer's forward product followed by its
+point-wise activation, and the activation gradient through it.
+
+mp_linear_fwd_act must give the bits of mp_linear_fwd (binary16 out) followed by
+mp_act_fwd, and mp_linear_dgrad_act the bits of mp_linear_dgrad followed by
+mp_act_bwd; each half is also checked against the oracle: the product within the
+binary16 GEMM tolerance (1e-2), ReLU exactly, GELU within one binary16 ulp of the
+oracle applied to the GPU's own product (two for the gradient).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_neural_amd as mp
+import oracle
+from gpu_util import dev_f16, f16_values, host_bits16, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_F16 = 1e-2
+
+
+def within_ulp(got_bits, ref_bits, ulps=1):
+    g, r = f16_values(got_bits), f16_values(ref_bits)
+    tol = np.maximum(np.abs(r) * 2.0 ** -10 * ulps, 2.0 ** -24 * ulps)
+    both_nan = np.isnan(g) & np.isnan(r)
+    same_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
+    return bool(np.all(both_nan | same_inf | (np.abs(g - r) <= tol)))
+
+
+def act_ref(kind, z):
+    return oracle.relu_fwd(z) if kind == mp.RELU else oracle.gelu_fwd(z)
+
+
+def act_grad_ref(kind, z, dy):
+    return oracle.relu_bwd(z, dy) if kind == mp.RELU else oracle.gelu_bwd(z, dy)
+
+
+def inputs(M, N, K, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((M, K)).astype(np.float16).view(np.uint16)
+    W = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float16).view(np.uint16)
+    dY = rng.standard_normal((M, N)).astype(np.float16).view(np.uint16)
+    Zs = rng.standard_normal((M, K)).astype(np.float16).view(np.uint16)   # saved pre-activation of dX
+    return X, W, dY, Zs
+
+
+def check_fwd(kind, X, W, Xd, Wd, Z=None, H=None, ref=True):
+    Z, H = mp.linear_fwd_act(kind, Xd, Wd, Z=Z, H=H)
+    Zu = mp.linear_fwd(Xd, Wd)
+    Hu = mp.act_fwd(kind, Zu)
+    torch.cuda.synchronize()
+    z, h = host_bits16(Z), host_bits16(H)
+    assert np.array_equal(z, host_bits16(Zu)), "Z differs from the unfused product"
+    assert np.array_equal(h, host_bits16(Hu)), "H differs from the unfused activation"
+    if ref:
+        assert rel_err(f16_values(z), oracle.linear_fwd(X, W)) <= TOL_F16
+    r = act_ref(kind, np.ascontiguousarray(z))
+    assert np.array_equal(h, r) if kind == mp.RELU else within_ulp(h, r)
+
+
+def check_dgrad(kind, dY, W, Zs, dYd, Wd, Zd, dZ=None, ref=True):
+    dZ = mp.linear_dgrad_act(kind, dYd, Wd, Zd, dZ=dZ)
+    dH = mp.linear_dgrad(dYd, Wd)
+    dZu = mp.act_bwd(kind, Zd.contiguous(), dH)
+    torch.cuda.synchronize()
+    out, dh = host_bits16(dZ), host_bits16(dH)
+    ref_u = host_bits16(dZu)
+    bad = np.argwhere(out != ref_u)
+    assert bad.size == 0, ("dZ differs from the unfused pair at %d of %d: " % (len(bad), out.size) +
+                           "; ".join("z=%04x dh=%04x fused=%04x unfused=%04x" % (
+                               host_bits16(Zd)[i, j], dh[i, j], out[i, j], ref_u[i, j]) for i, j in bad[:12]))
+    if ref:
+        assert rel_err(f16_values(dh), oracle.linear_dgrad(dY, W)) <= TOL_F16
+    r = act_grad_ref(kind, np.ascontiguousarray(Zs), dh)
+    assert np.array_equal(out, r) if kind == mp.RELU else within_ulp(out, r, ulps=2)
+
+
+@pytest.mark.parametrize("kind", [mp.RELU, mp.GELU])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (64, 512, 256), (64, 10, 512), (300, 520, 200),
+                                   (777, 1000, 333), (2600, 3100, 96), (1280, 1024, 384)])
+def test_fused_matches_unfused_and_oracle(kind, M, N, K):
+    """Small (64 x 64 tiles) and large (256 x 256 tiles) grids, ragged in every dimension."""
+    require_gpu()
+    X, W, dY, Zs = inputs(M, N, K, M * 5 + N * 3 + K + kind)
+    Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
+    check_fwd(kind, X, W, Xd, Wd)
+    check_dgrad(kind, dY, W, Zs, dYd, Wd, Zd)
+
+
+@pytest.mark.parametrize("kind", [mp.RELU, mp.GELU])
+def test_fused_unaligned_and_strided(kind):
+    """Row pitches that are not multiples of 8 and outputs inside wider buffers take the
+    element-wise epilogue; nothing beyond the output columns is written."""
+    require_gpu()
+    M, N, K = 333, 270, 77
+    X, W, dY, Zs = inputs(M, N, K + 0, 9 + kind)
+    Xf = np.zeros((M, K + 3), np.uint16); Xf[:, :K] = X
+    Wf = np.zeros((N, K + 5), np.uint16); Wf[:, :K] = W
+    Zf = np.zeros((M, K + 1), np.uint16); Zf[:, :K] = Zs
+    Xd, Wd, Zd = dev_f16(Xf)[:, :K], dev_f16(Wf)[:, :K], dev_f16(Zf)[:, :K]
+    Zbuf = torch.full((M, N + 9), 7.0, dtype=torch.float16, device="cuda")
+    Hbuf = torch.full((M, N + 1), 7.0, dtype=torch.float16, device="cuda")
+    check_fwd(kind, X, W, Xd, Wd, Z=Zbuf[:, :N], H=Hbuf[:, :N])
+    assert (Zbuf[:, N:] == 7.0).all() and (Hbuf[:, N:] == 7.0).all()
+    dZbuf = torch.full((M, K + 2), 7.0, dtype=torch.float16, device="cuda")
+    check_dgrad(kind, dY, W, Zs, dev_f16(dY), Wd, Zd, dZ=dZbuf[:, :K])
+    assert (dZbuf[:, K:] == 7.0).all()
+
+
+def test_fused_c4_layer_shape():
+    """The benchmark's launch configuration: one 4096^3 GELU layer. Bitwise equal to the unfused
+    pair over all 16.8M outputs; the activation checked against the oracle on all of them."""
+    require_gpu()
+    n = 4096
+    X, W, dY, Zs = inputs(n, n, n, 4096)
+    Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
+    check_fwd(mp.GELU, X, W, Xd, Wd, ref=False)
+    check_dgrad(mp.GELU, dY, W, Zs, dYd, Wd, Zd, ref=False)
+
+
+def test_fused_argument_errors():
+    require_gpu()
+    a = torch.zeros((8, 8), dtype=torch.float16, device="cuda")
+    with pytest.raises(mp.MPError):
+        mp.linear_fwd_act(7, a, a)
+    with pytest.raises(mp.MPError):
+        mp.linear_dgrad_act(-1, a, a, a)
+    with pytest.raises(ValueError):
+        mp.linear_dgrad_act(mp.GELU, a, a, torch.zeros((8, 4), dtype=torch.float16, device="cuda"))

@@ -110,6 +110,22 @@ def test_ragged_shapes_against_oracle(M, N, K):
         assert rel_err(f16_values(g), r) <= TOL_F16, name
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 10, 512), (300, 520, 200), (1280, 1024, 384), (2048, 2048, 1024)])
+def test_binary16_output_is_nearest_even_of_the_fp32_output(M, N, K):
+    """The binary16 epilogue rounds the FP32 accumulator to nearest even (§3.4: FP32 sums,
+    rounded to binary16 when stored): both outputs come from the same accumulation, so the
+    binary16 result must equal the oracle's RNE of the FP32 result bit for bit, ties included."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(M + 3 * N + 7 * K))
+    X = rng.standard_normal((M, K)).astype(np.float16).view(np.uint16)
+    W = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float16).view(np.uint16)
+    dY = rng.standard_normal((M, N)).astype(np.float16).view(np.uint16)
+    f32 = gpu_all(X, W, dY, torch.float32)
+    f16 = gpu_all(X, W, dY, torch.float16)
+    for a, b, name in zip(f32, f16, ("fwd", "dgrad", "wgrad")):
+        assert np.array_equal(b, oracle.f32_to_f16(np.ascontiguousarray(a))), name
+
+
 def test_unaligned_leading_dimensions():
     """Row pitches that are not multiples of 8 elements take the element-wise load path."""
     require_gpu()

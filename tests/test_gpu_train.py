@@ -46,9 +46,10 @@ def oracle_c1(cfg, steps, scale=None):
     return losses, flags, W, S
 
 
-def gpu_c1(cfg, steps, scale=None, prechecked=False):
+def gpu_c1(cfg, steps, scale=None, prechecked=False, fused=False):
     """prechecked: the weight-gradient GEMMs set the scaler's overflow flag in their epilogue and
-    the sweep skips its own check pass (Step 6 fused into the producer)."""
+    the sweep skips its own check pass (Step 6 fused into the producer). fused: the ReLU and its
+    gradient run in the epilogues of the forward and dgrad products."""
     S = mp.Scaler(scale or cfg.scale, cfg.dynamic, cfg.growth_interval)
     W = [dev_f32(cfg.W1), dev_f32(cfg.W2)]
     V = [torch.zeros_like(w) for w in W]
@@ -64,14 +65,20 @@ def gpu_c1(cfg, steps, scale=None, prechecked=False):
     loss = torch.empty(1, dtype=torch.float32, device="cuda")
     losses, flags = [], []
     for _ in range(steps):
-        mp.linear_fwd(X, W16[0], Y=Z1)
-        mp.act_fwd(mp.RELU, Z1, H1)
+        if fused:
+            mp.linear_fwd_act(mp.RELU, X, W16[0], Z=Z1, H=H1)
+        else:
+            mp.linear_fwd(X, W16[0], Y=Z1)
+            mp.act_fwd(mp.RELU, Z1, H1)
         mp.linear_fwd(H1, W16[1], Y=Z2)
         mp.loss_softmax_ce(Z2, y, S, loss, dZ2)
         fi = S.found_inf_ptr if prechecked else None
         mp.linear_wgrad(dZ2, H1, dW=G[1], found_inf=fi)
-        mp.linear_dgrad(dZ2, W16[1], dX=dH1)
-        mp.act_bwd(mp.RELU, Z1, dH1, dZ1)
+        if fused:
+            mp.linear_dgrad_act(mp.RELU, dZ2, W16[1], Z1, dZ=dZ1)
+        else:
+            mp.linear_dgrad(dZ2, W16[1], dX=dH1)
+            mp.act_bwd(mp.RELU, Z1, dH1, dZ1)
         mp.linear_wgrad(dZ1, X, dW=G[0], found_inf=fi)
         mp.step(pl, S, cfg.lr, cfg.momentum, cfg.weight_decay,
                 flags=mp.MP_GRADS_PRECHECKED if prechecked else 0)
@@ -113,3 +120,18 @@ def test_c1_absurd_scale_overflows_and_skips(prechecked):
     assert o_flags == g_flags == [1, 1]
     assert np.array_equal(g_W[0], cfg.W1) and np.array_equal(g_W[1], cfg.W2)
     assert g_S["skipped_steps"] == o_S.skipped_steps == 2 and g_S["scale"] == 2.0 ** 40
+
+
+def test_c1_fused_activation_layers_give_the_same_bits():
+    """The fused forward/dgrad epilogues reproduce the unfused step exactly: the same losses,
+    the same flags and bit-identical masters after 10 steps; and still match the oracle run."""
+    require_gpu()
+    cfg = workloads.c1()
+    u_loss, u_flags, (u_W, u_S) = gpu_c1(cfg, cfg.steps, prechecked=True)
+    f_loss, f_flags, (f_W, f_S) = gpu_c1(cfg, cfg.steps, prechecked=True, fused=True)
+    assert f_loss == u_loss and f_flags == u_flags
+    for a, b in zip(f_W, u_W):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    o_loss, _, _, _ = oracle_c1(cfg, cfg.steps)
+    for a, b in zip(f_loss, o_loss):
+        assert math.isclose(a, b, rel_tol=1e-2)
