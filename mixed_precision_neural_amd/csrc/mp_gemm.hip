@@ -358,6 +358,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
     static_assert(WTM % kRowsPerPass == 0, "whole passes");
     uint32_t bad = 0;
     uint8_t* stage = reinterpret_cast<uint8_t*>(lds) + size_t(wave) * WTM * WTN * 2;
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    // Whole wave tiles with 16-byte access everywhere take an unchecked path.
+    const bool whole = g.c_vec && (EPI == kEpiF16 || g.aux_vec) && wrow0 + WTM <= g.Mc &&
+                       wcol0 + WTN <= g.Nc;
+    // Read-back passes in groups; the dgrad epilogue's saved pre-activation
+    // values for a group are loaded one group ahead, the first group before the
+    // staging writes, so their latency overlaps other work.
+    constexpr int kPasses = WTM / kRowsPerPass;
+    constexpr int kGrp = kPasses < 4 ? kPasses : 4;
+    static_assert(kPasses % kGrp == 0, "whole groups");
+    auto piece_row = [&](int p) { return p * kRowsPerPass + lane / kChunks; };
+    auto piece_chunk = [&]() { return lane % kChunks; };
+    uint4 za[kGrp], zb[kGrp];
+    auto zload = [&](uint4 (&z)[kGrp], int p0) {
+#pragma unroll
+        for (int q = 0; q < kGrp; ++q)
+            z[q] = *reinterpret_cast<const uint4*>(g.Z + (wrow0 + piece_row(p0 + q)) * g.ldz + wcol0 +
+                                                   8 * piece_chunk());
+    };
+    if (EPI == kEpiDact && whole) zload(za, 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -373,34 +393,53 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
                                           8 * (lane >> 5)) = v;
             }
     __syncthreads();
-    uint16_t* C = static_cast<uint16_t*>(g.C);
-#pragma unroll 4
-    for (int p = 0; p < WTM / kRowsPerPass; ++p) {
-        const int m = p * kRowsPerPass + lane / kChunks, c = lane % kChunks;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16);
-        const int64_t gr = wrow0 + m, gc = wcol0 + 8 * c;
-        if (gr >= g.Mc) continue;
-        uint16_t* dst = C + gr * g.ldc + gc;
-        if (g.c_vec && gc + 8 <= g.Nc && (EPI == kEpiF16 || g.aux_vec)) {
-            if (EPI == kEpiF16) {
-                *reinterpret_cast<uint4*>(dst) = v;
-                bad |= mp::nonfinite2(v.x) | mp::nonfinite2(v.y) | mp::nonfinite2(v.z) | mp::nonfinite2(v.w);
-            } else if (EPI == kEpiAct) {
-                *reinterpret_cast<uint4*>(dst) = v;
-                uint16_t a[8];
+    auto staged = [&](int m, int c) {
+        return *reinterpret_cast<const uint4*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16);
+    };
+    if (whole) {
+        auto group = [&](const uint4 (&z)[kGrp], int p0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = mp::act_fwd1<KIND>(half_of(v, e));
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
-                    make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
-            } else {
-                const uint4 z = *reinterpret_cast<const uint4*>(g.Z + gr * g.ldz + gc);
-                uint16_t d[8];
+            for (int q = 0; q < kGrp; ++q) {
+                const int m = piece_row(p0 + q), c = piece_chunk();
+                const uint4 v = staged(m, c);
+                const int64_t gr = wrow0 + m, gc = wcol0 + 8 * c;
+                uint16_t* dst = C + gr * g.ldc + gc;
+                if (EPI == kEpiF16) {
+                    *reinterpret_cast<uint4*>(dst) = v;
+                    bad |= mp::nonfinite2(v.x) | mp::nonfinite2(v.y) | mp::nonfinite2(v.z) | mp::nonfinite2(v.w);
+                } else if (EPI == kEpiAct) {
+                    *reinterpret_cast<uint4*>(dst) = v;
+                    uint16_t a[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d[e] = epi_main<EPI, KIND>(half_of(v, e), half_of(z, e));
-                *reinterpret_cast<uint4*>(dst) =
-                    make_uint4(pack2(d[0], d[1]), pack2(d[2], d[3]), pack2(d[4], d[5]), pack2(d[6], d[7]));
+                    for (int e = 0; e < 8; ++e) a[e] = mp::act_fwd1<KIND>(half_of(v, e));
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
+                        make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+                } else {
+                    uint16_t d[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] = epi_main<EPI, KIND>(half_of(v, e), half_of(z[q], e));
+                    *reinterpret_cast<uint4*>(dst) =
+                        make_uint4(pack2(d[0], d[1]), pack2(d[2], d[3]), pack2(d[4], d[5]), pack2(d[6], d[7]));
+                }
             }
-        } else {
+        };
+#pragma unroll 1
+        for (int p0 = 0; p0 < kPasses; p0 += 2 * kGrp) {
+            if (EPI == kEpiDact && p0 + kGrp < kPasses) zload(zb, p0 + kGrp);
+            group(za, p0);
+            if (p0 + kGrp < kPasses) {
+                if (EPI == kEpiDact && p0 + 2 * kGrp < kPasses) zload(za, p0 + 2 * kGrp);
+                group(zb, p0 + kGrp);
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int p = 0; p < kPasses; ++p) {
+            const int m = piece_row(p), c = piece_chunk();
+            const uint4 v = staged(m, c);
+            const int64_t gr = wrow0 + m, gc = wcol0 + 8 * c;
+            if (gr >= g.Mc) continue;
+            uint16_t* dst = C + gr * g.ldc + gc;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (gc + e < g.Nc) {
