@@ -28,15 +28,22 @@
 //     of the four 8-byte pieces its group reads, i.e. four reduction values of
 //     one index column.
 // Both swizzles keep the fragment reads of the 256-wide tiles free of LDS bank
-// conflicts. For whole tiles the steady-state slice loop has no branches and
-// an explicit instruction order: in sub-step 0 every MFMA is paired with a
-// global load, in sub-steps 0-2 with the LDS reads of the next sub-step, in
-// sub-step 3 with an LDS store of the next slice, so memory traffic issues
-// while the matrix cores run instead of between their bursts.
+// conflicts. Whole 256 x 256 tiles take a loop unrolled over the two LDS
+// stages, with buffer loads (scalar slab offsets) and fragment addresses that
+// are a few per-lane registers plus immediates, and an explicit instruction
+// order: in sub-step 0 every MFMA is paired with a global load, in sub-steps
+// 0-2 with the LDS reads of the next sub-step, in sub-step 3 with an LDS store
+// of the next slice, so memory traffic issues while the matrix cores run
+// instead of between their bursts. Edge tiles and small grids use a general
+// loop with clamped, zero-filled loads.
 // Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
 // 8 XCDs) works on a compact group of tiles that share rows of A and B in its
-// own L2.
+// own L2. Binary16 outputs are rounded into LDS and written back as whole
+// 16-byte row pieces; the activation-fused modes apply the point-wise step to
+// those pieces.
 #include "mp_internal.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -62,6 +69,7 @@ struct GemmArgs {
     const uint16_t* Z;           // kEpiDact: saved pre-activation (binary16), ldz
     int64_t ldc2, ldz;
     int aux_vec;                 // 16-byte access allowed for C2 / Z
+    int pipe_ok;                 // operand panels under 4 GB: the buffer-load main loop applies
     int tiles_m, tiles_n;
 };
 
@@ -263,6 +271,216 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
     }
 }
 
+// One operand's slab (ROWS index rows x 64 reduction elements) fetched with
+// buffer loads: a resource over the operand's panel in scalar registers, a
+// fixed 32-bit byte offset per chunk in a vector register, and a scalar offset
+// per slab, so the loop does no vector address arithmetic. Chunk u of a thread
+// is the TileLoader's chunk tid + 256 u; its LDS address is one of two
+// per-lane values (KC: the swizzle of rows 32 apart differs in bit 2) plus
+// the immediate 4096 u.
+template <int ROWS, int NT, bool KC>
+struct PipeLoader {
+    static constexpr int kPer = ROWS * kRowChunks / NT;
+    static constexpr int C = ROWS / 8;                       // 16-byte chunks per MN row
+    static_assert(NT == 256 && ROWS == 256, "chunk u of a thread is 32 KC rows / 8 MN rows further");
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff[kPer];
+    uint32_t lds0, lds1;
+    mp::u32x4 r[kPer];
+
+    // panel: A(row0, 0) for KC, A(0, row0) for MN; lds_base: byte offset of the operand's stage 0
+    __device__ __forceinline__ void init(const uint16_t* panel, int64_t ld, int tid, uint32_t lds_base) {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(panel), 0, -1, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + u * NT;
+            if (KC) voff[u] = uint32_t(((q / kRowChunks) * ld + (q % kRowChunks) * 8) * 2);
+            else voff[u] = uint32_t(((q / C) * ld + (q % C) * 8) * 2);
+        }
+        if (KC) {
+            const int row = tid / kRowChunks, kc = tid % kRowChunks;
+            lds0 = lds_base + uint32_t(row * 128 + 16 * (kc ^ swz_kc(row)));
+            lds1 = lds_base + uint32_t(row * 128 + 16 * (kc ^ swz_kc(row) ^ 4));
+        } else {
+            const int k = tid / C, cb = tid % C;
+            lds0 = lds1 = lds_base + uint32_t((k * C + (cb ^ swz_mn<C>(k))) * 16);
+        }
+    }
+    // soff: byte offset of the slab within the panel
+    __device__ __forceinline__ void fetch(uint32_t soff) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            r[u] = __builtin_bit_cast(mp::u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[u], soff, 0));
+    }
+    __device__ __forceinline__ void store(__attribute__((address_space(3))) uint8_t* lds, uint32_t stage_off) const {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            *reinterpret_cast<__attribute__((address_space(3))) mp::u32x4*>(
+                lds + ((u & 1) ? lds1 : lds0) + 4096 * u + stage_off) = r[u];
+    }
+};
+
+// Per-lane LDS byte addresses of one operand's MFMA fragments, folded so that
+// everything but the lane-dependent XOR swizzle is an immediate offset of the
+// ds_read (the stage, the 32-row block pairs, the reduction sub-step):
+//   KC: fragment (i, kk) of a wave's rows R0 + 32 i + (lane & 31) sits at
+//       row * 128 + 16 * ((2 kk + lane / 32) ^ swz_kc(row)); for rows 32 apart
+//       the swizzle differs only in bit 2 (i odd), so 8 addresses (kk, i & 1)
+//       cover all 16, plus 4096 i.
+//   MN: fragment (j, kk) reads reduction rows 16 kk + ...; the chunk swizzle
+//       depends only on the lane, so 8 addresses (j, h) plus kk * 256 * ROWS/8
+//       cover all, h being the two transposing reads of a fragment.
+typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <int ROWS, bool KC>
+struct FragAddr {
+    uint32_t a[8];
+    // r0w: first index row of the wave's block; base: byte offset of the operand's stage 0
+    __device__ __forceinline__ void init(int r0w, int lane, uint32_t base) {
+        if (KC) {
+            const int l = lane & 31, h = lane >> 5;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    a[kk * 2 + p] = base + uint32_t((r0w + l) * 128 + 16 * ((2 * kk + h) ^ swz_kc(l) ^ (4 * p)));
+        } else {
+            constexpr int C = ROWS / 8;
+            const int g4 = lane >> 4, ii = lane & 15;
+            const int sw = swz_mn<C>(ii >> 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = r0w + 32 * j + 16 * (g4 & 1) + 4 * (ii & 3);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    a[j * 2 + h] = base + uint32_t((8 * (g4 >> 1) + 4 * h + (ii >> 2)) * C * 16 +
+                                                   16 * ((n >> 3) ^ sw) + 8 * (ii & 1));
+            }
+        }
+    }
+    // fragment idx (i for KC rows, j for MN columns) of sub-step kk; off: stage offset in bytes
+    __device__ __forceinline__ half8 read(lds_u8* lds, int idx, int kk, uint32_t off) const {
+        if (KC) {
+            return *reinterpret_cast<const __attribute__((address_space(3))) half8*>(
+                lds + a[kk * 2 + (idx & 1)] + 4096 * idx + off);
+        } else {
+            constexpr uint32_t kStep = 256 * (ROWS / 8);     // bytes per 16 reduction rows
+            short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4*)(lds + a[idx * 2 + 0] + kk * kStep + off));
+            short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4*)(lds + a[idx * 2 + 1] + kk * kStep + off));
+            const short8_t w = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            return __builtin_bit_cast(half8, w);
+        }
+    }
+};
+
+// The reduction loop for whole 256 x 256 tiles (reduction a multiple of 64,
+// 16-byte aligned rows, panels under 4 GB). LDS holds two stages per operand:
+// A's at 0 and 32 KB, B's at 64 KB and 96 KB; slab kt lives in stage kt & 1.
+// The loop is unrolled over the two stages, so every LDS address is one of a
+// few per-lane registers plus an immediate, and the loads are buffer loads
+// with a scalar slab offset: no vector address arithmetic per slab. Each slab
+// fetches the next one into registers under its first sub-step and stores it
+// into the other stage under its last, then a barrier.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int FM, int FN>
+__device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* lds, int64_t row0, int64_t col0,
+                                                 int tid, int lane, int wm, int wn, floatx16 (&acc)[FM][FN]) {
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr uint32_t kAStage = BM * kRowChunks * 16, kBStage = BN * kRowChunks * 16;   // bytes
+    constexpr uint32_t kBBase = 2 * kAStage;
+    constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per sub-step
+    using LA = PipeLoader<BM, NT, A_KC>;
+    using LB = PipeLoader<BN, NT, B_KC>;
+    constexpr int kLoads = LA::kPer + LB::kPer;                          // loads / stores per thread
+    static_assert(FM == 4 && FN == 4 && WTM == 128 && WTN == 128, "4 x 4 blocks of 32 x 32 per wave");
+    static_assert(kReads <= 16 && kLoads <= 16, "one sub-step = 16 MFMAs");
+    static_assert(kAStage <= 32768 && kBStage <= 32768, "stage offsets must fit the LDS immediate");
+    const int nk = int(g.R / kBK);
+    lds_u8* l8 = (lds_u8*)(lds);
+    __attribute__((address_space(3))) uint8_t* w8 = (__attribute__((address_space(3))) uint8_t*)(lds);
+    LA la;
+    LB lb;
+    la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, tid, 0);
+    lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, tid, kBBase);
+    FragAddr<BM, A_KC> fa;
+    FragAddr<BN, B_KC> fb;
+    fa.init(wm * WTM, lane, 0);
+    fb.init(wn * WTN, lane, kBBase);
+    // byte offset of slab kt within a panel: 64 elements along a KC row, 64 rows of an MN panel
+    const uint32_t a_step = A_KC ? 2 * kBK : uint32_t(2 * kBK * g.lda);
+    const uint32_t b_step = B_KC ? 2 * kBK : uint32_t(2 * kBK * g.ldb);
+    auto fetch = [&](int kt) {
+        la.fetch(uint32_t(kt) * a_step);
+        lb.fetch(uint32_t(kt) * b_step);
+    };
+    auto store = [&](int stage) {
+        la.store(w8, stage * kAStage);
+        lb.store(w8, stage * kBStage);
+    };
+    auto read_frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = fa.read(l8, i, kk, stage * kAStage);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = fb.read(l8, j, kk, stage * kBStage);
+    };
+    auto mfma = [&](const half8 (&af)[FM], const half8 (&bf)[FN], int from, int to) {
+#pragma unroll
+        for (int t = from; t < to; ++t)
+            acc[t / FN][t % FN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[t % FN], af[t / FN], acc[t / FN][t % FN], 0, 0, 0);
+    };
+
+    half8 af[2][FM], bf[2][FN];
+    // Prologue: slab 0 in stage 0.
+    fetch(0);
+    store(0);
+    __syncthreads();
+
+    // One slab in stage S; NEXT: slab kt + 1 exists and is fetched now, stored
+    // into the other stage under the last sub-step.
+    auto slab = [&](int kt, auto s_tag, auto next_tag) {
+        constexpr int S = decltype(s_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
+        if constexpr (NEXT) fetch(kt + 1);
+        read_frags(S, 0, af[0], bf[0]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk < 3) read_frags(S, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+            mfma(af[kk & 1], bf[kk & 1], 0, 16);
+        }
+        if constexpr (NEXT) store(S ^ 1);
+        // Instruction order (groups are filled in program order): the first
+        // fragments, then each MFMA paired with a load (sub-step 0), the next
+        // sub-step's fragment reads (0-2) and a store of the next slab (3).
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+        for (int kk = 0; kk < 4; ++kk)
+            for (int m = 0; m < 16; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (NEXT && kk == 0 && m < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (kk < 3 && m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (NEXT && kk == 3 && m < kLoads) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
+        __syncthreads();
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using T = std::true_type;
+    using F = std::false_type;
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {                  // steady state: no branches inside
+        slab(kt, C0(), T());
+        slab(kt + 1, C1(), T());
+    }
+    // the last 1 or 2 slabs (kt is even here)
+    if (nk - kt == 2) {
+        slab(kt, C0(), T());
+        slab(kt + 1, C1(), F());
+    } else {
+        slab(kt, C0(), F());
+    }
+}
+
 // Applies the binary16 point-wise tail of the epilogue to one output element
 // h = RNE16(acc) and stores it (z: the saved pre-activation, kEpiDact only).
 template <int EPI, int KIND>
@@ -312,7 +530,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
 
     const bool full = g.a_vec && g.b_vec && (g.R % kBK) == 0 && row0 + BM <= g.Mc &&
                       col0 + BN <= g.Nc;
-    if (full)
+    bool done = false;
+    if constexpr (BM == 256 && BN == 256) {
+        if (full && g.pipe_ok) {
+            reduce_tile_pipe<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, FM, FN>(g, lds, row0, col0, tid, lane, wm, wn, acc);
+            done = true;
+        }
+    }
+    if (done) {
+    } else if (full)
         reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, true, FM, FN>(g, lds, row0, col0, tid, lane,
                                                                       wm, wn, acc);
     else
@@ -465,6 +691,12 @@ template <int BM, int BN, int WM, int WN, bool A_KC, bool B_KC, int EPI, int KIN
 mp_status launch_cfg(GemmArgs a, hipStream_t s, const char* name) {
     a.tiles_m = int((a.Mc + BM - 1) / BM);
     a.tiles_n = int((a.Nc + BN - 1) / BN);
+    // buffer-load offsets within an operand's panel must stay below 2^32 bytes
+    const auto panel_ok = [&](bool kc, int64_t ld) {
+        const int64_t bytes = kc ? (int64_t(BM > BN ? BM : BN) * ld + a.R) * 2 : (a.R + 64) * ld * 2 + 512;
+        return bytes < (int64_t(1) << 32);
+    };
+    a.pipe_ok = int(panel_ok(A_KC, a.lda) && panel_ok(B_KC, a.ldb));
     const uint32_t blocks = uint32_t(a.tiles_m) * uint32_t(a.tiles_n);
     gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, EPI, KIND><<<blocks, 64 * WM * WN, 0, s>>>(a);
     return mp::launch_status(name);
