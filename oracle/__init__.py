@@ -72,6 +72,15 @@ def lib():
         L.or_sgd_update.argtypes = [vp, i32, C.c_float, C.c_float, C.c_float, C.c_float]
         L.or_step.argtypes = [vp, i32, C.c_float, C.c_float, C.c_float, C.c_float]
         L.or_step.restype = C.c_uint32
+        L.or_opt_update.argtypes = [vp, i32, i32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_float]
+        L.or_step_opt.argtypes = [vp, i32, i32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_float]
+        L.or_step_opt.restype = C.c_uint32
+        L.or_absmax_f32.argtypes = [vp, i64, C.c_float, C.POINTER(C.c_uint32)]
+        L.or_absmax_f32.restype = C.c_float
+        L.or_absmax_f16.argtypes = [vp, i64, C.c_float, C.POINTER(C.c_uint32)]
+        L.or_absmax_f16.restype = C.c_float
+        L.or_scale_from_absmax.argtypes = [C.c_float, C.c_float]
+        L.or_scale_from_absmax.restype = C.c_float
         L.or_scaler_init.argtypes = [C.POINTER(Scaler), C.c_float, i32, i32]
         L.or_scaler_update.argtypes = [C.POINTER(Scaler)]
         L.or_relu_fwd.argtypes = [u16p, u16p, i64]
@@ -218,6 +227,42 @@ def step(masters, moms, grads, w16s, lr, momentum, weight_decay, inv_scale) -> i
     """Check, then update in place only when no gradient is +-inf/NaN. Returns the flag."""
     arr, n = _params(masters, moms, grads, w16s)
     return int(lib().or_step(arr, n, lr, momentum, weight_decay, inv_scale))
+
+
+SGD, NESTEROV, ADAGRAD = 0, 1, 2      # optimizer kinds of the sweep
+
+
+def opt_update(kind, masters, moms, grads, w16s, lr, momentum, weight_decay, eps, inv_scale):
+    """The update rule `kind` on every element, unconditionally (moms: v, or G for Adagrad)."""
+    arr, n = _params(masters, moms, grads, w16s)
+    lib().or_opt_update(arr, n, int(kind), lr, momentum, weight_decay, eps, inv_scale)
+
+
+def step_opt(kind, masters, moms, grads, w16s, lr, momentum, weight_decay, eps, inv_scale) -> int:
+    """Check, then the update rule `kind` in place when no gradient is +-inf/NaN. Returns the flag."""
+    arr, n = _params(masters, moms, grads, w16s)
+    return int(lib().or_step_opt(arr, n, int(kind), lr, momentum, weight_decay, eps, inv_scale))
+
+
+def absmax(tensors, running: float = 0.0):
+    """(max(running, max |x| over the finite elements), 1 if any element is +-inf/NaN else 0)
+    over a list of float32 arrays or binary16 bit-pattern (uint16) arrays."""
+    nonfinite = C.c_uint32(0)
+    m = float(running)
+    for t in tensors:
+        t = np.ascontiguousarray(t)
+        if t.dtype == np.float32:
+            m = lib().or_absmax_f32(_p(t), t.size, m, C.byref(nonfinite))
+        elif t.dtype == np.uint16:
+            m = lib().or_absmax_f16(_p(t), t.size, m, C.byref(nonfinite))
+        else:
+            raise TypeError("absmax takes float32 or uint16 (binary16 bits) arrays")
+    return float(m), int(nonfinite.value)
+
+
+def scale_from_absmax(amax: float, headroom: float = 2.0) -> float:
+    """Largest power of two S with S * headroom * amax <= 65504, within [1, 2^64]."""
+    return float(lib().or_scale_from_absmax(amax, headroom))
 
 
 def scaler_init(init_scale, dynamic, growth_interval) -> Scaler:

@@ -275,6 +275,8 @@ typedef struct {
     const int64_t* first;      /* prefix sums of numel                */
     float lr, mu, wd, inv_scale;
     uint32_t flag;             /* OR of every range's check result    */
+    int32_t kind;              /* OR_OPT_*                            */
+    float eps;                 /* Adagrad's denominator term          */
 } step_ctx;
 
 static int find_tensor(const step_ctx* s, int64_t gidx) {
@@ -300,10 +302,25 @@ static void update_range(int64_t lo, int64_t hi, void* p) {
         float g  = gs * s->inv_scale;           /* Step 5: unscale        */
         float t1 = s->wd * w;                   /* weight decay term      */
         g = g + t1;
-        float t2 = s->mu * v;                   /* Step 7: momentum       */
-        v = t2 + g;
-        float t3 = s->lr * v;                   /* Step 7: master update  */
-        w = w - t3;
+        if (s->kind == OR_OPT_ADAGRAD) {
+            float t2 = g * g;                   /* accumulate g^2         */
+            v = v + t2;
+            float r = sqrtf(v);
+            float d = r + s->eps;
+            float u = g / d;
+            float t3 = s->lr * u;
+            w = w - t3;
+        } else {
+            float t2 = s->mu * v;               /* Step 7: momentum       */
+            v = t2 + g;
+            float step = v;
+            if (s->kind == OR_OPT_NESTEROV) {   /* look-ahead: g + mu v   */
+                float t4 = s->mu * v;
+                step = g + t4;
+            }
+            float t3 = s->lr * step;            /* Step 7: master update  */
+            w = w - t3;
+        }
         q->master[i] = w;
         q->momentum[i] = v;
         q->weight16[i] = or_f32_to_f16(w);      /* Step 1: nearest FP16   */
@@ -337,7 +354,7 @@ static int64_t total_numel(const int64_t* first, const or_param* params, int32_t
 uint32_t or_check_overflow(const or_param* params, int32_t n) {
     if (n <= 0) return 0;
     int64_t* first = prefix_numel(params, n);
-    step_ctx s = { params, n, first, 0, 0, 0, 0, 0 };
+    step_ctx s = { params, n, first, 0, 0, 0, 0, 0, OR_OPT_SGD, 0.0f };
     parallel_for(total_numel(first, params, n), 1 << 16, check_range, &s);
     free(first);
     return s.flag;
@@ -347,9 +364,25 @@ void or_sgd_update(const or_param* params, int32_t n, float lr, float momentum,
                    float weight_decay, float inv_scale) {
     if (n <= 0) return;
     int64_t* first = prefix_numel(params, n);
-    step_ctx s = { params, n, first, lr, momentum, weight_decay, inv_scale, 0 };
+    step_ctx s = { params, n, first, lr, momentum, weight_decay, inv_scale, 0, OR_OPT_SGD, 0.0f };
     parallel_for(total_numel(first, params, n), 1 << 16, update_range, &s);
     free(first);
+}
+
+void or_opt_update(const or_param* params, int32_t n, int32_t kind, float lr, float momentum,
+                   float weight_decay, float eps, float inv_scale) {
+    if (n <= 0) return;
+    int64_t* first = prefix_numel(params, n);
+    step_ctx s = { params, n, first, lr, momentum, weight_decay, inv_scale, 0, kind, eps };
+    parallel_for(total_numel(first, params, n), 1 << 16, update_range, &s);
+    free(first);
+}
+
+uint32_t or_step_opt(const or_param* params, int32_t n, int32_t kind, float lr, float momentum,
+                     float weight_decay, float eps, float inv_scale) {
+    uint32_t flag = or_check_overflow(params, n);
+    if (!flag) or_opt_update(params, n, kind, lr, momentum, weight_decay, eps, inv_scale);
+    return flag;
 }
 
 uint32_t or_step(const or_param* params, int32_t n, float lr, float momentum,
@@ -357,6 +390,47 @@ uint32_t or_step(const or_param* params, int32_t n, float lr, float momentum,
     uint32_t flag = or_check_overflow(params, n);
     if (!flag) or_sgd_update(params, n, lr, momentum, weight_decay, inv_scale);
     return flag;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Loss-scale method 2 ([A] §3.4, the direct statistical approach).            */
+/* ------------------------------------------------------------------------- */
+
+float or_absmax_f32(const float* x, int64_t n, float running, uint32_t* nonfinite) {
+    float m = running;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(x[i])) {
+            if (nonfinite) *nonfinite = 1;
+            continue;
+        }
+        float a = fabsf(x[i]);
+        if (a > m) m = a;
+    }
+    return m;
+}
+
+float or_absmax_f16(const uint16_t* x, int64_t n, float running, uint32_t* nonfinite) {
+    float m = running;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = or_f16_to_f32(x[i]);
+        if (!isfinite(v)) {
+            if (nonfinite) *nonfinite = 1;
+            continue;
+        }
+        float a = fabsf(v);
+        if (a > m) m = a;
+    }
+    return m;
+}
+
+float or_scale_from_absmax(float amax, float headroom) {
+    /* S = 2^64 down to 1: the first S with S * headroom * amax <= 65504. With
+       power-of-two S and headroom both products are exact (or overflow to
+       +inf, which fails the test), so the comparison is exact. */
+    float x = headroom * amax;
+    float S = ldexpf(1.0f, 64);
+    while (S > 1.0f && S * x > 65504.0f) S = S * 0.5f;
+    return S;
 }
 
 /* ------------------------------------------------------------------------- */

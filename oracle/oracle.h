@@ -73,6 +73,36 @@ void or_sgd_update(const or_param* params, int32_t n, float lr, float momentum,
 uint32_t or_step(const or_param* params, int32_t n, float lr, float momentum,
                  float weight_decay, float inv_scale);
 
+/* ---- optimizer variants of the same sweep ----
+ * The pages name the optimizers their experiments used but print no update
+ * rule for them: Nesterov-momentum SGD ([A] §3.1 "Empirical validation
+ * (Figure 2a)", §4.3, §6.4) and Adagrad ([A] §4.5 (Figure 5), §6.4). The rules
+ * below are the textbook forms (readings, see the test-suite's pins):
+ *   OR_OPT_SGD       v = mu v + g;           w = w - lr v
+ *   OR_OPT_NESTEROV  v = mu v + g;           w = w - lr (g + mu v)
+ *   OR_OPT_ADAGRAD   G = G + g g;            w = w - lr (g / (sqrt(G) + eps))
+ * with g = g16 / S + weight_decay w, every operation one IEEE FP32 rounding in
+ * the order written (sqrt and division correctly rounded), `momentum` holding
+ * v or G. Steps 5, 6 and 1 are as for or_step.                              */
+enum { OR_OPT_SGD = 0, OR_OPT_NESTEROV = 1, OR_OPT_ADAGRAD = 2 };
+void or_opt_update(const or_param* params, int32_t n, int32_t kind, float lr, float momentum,
+                   float weight_decay, float eps, float inv_scale);
+uint32_t or_step_opt(const or_param* params, int32_t n, int32_t kind, float lr, float momentum,
+                     float weight_decay, float eps, float inv_scale);
+
+/* ---- loss-scale method 2, [A] §3.4 "Choosing the scaling factor — the direct
+ * statistical approach" and the gradient-statistics recipe after it:
+ * record g_max = max |gradient| over all layers (and iterations), then
+ * S = 65504 / (h g_max), h = 2 leaving one bit of headroom.
+ * or_absmax_*: max(running, max |x| over the finite elements of x); any
+ * +-inf/NaN element sets *nonfinite (when not NULL) and is left out.
+ * or_scale_from_absmax: the largest power of two S with S h amax <= 65504
+ * (a power of two keeps the unscale exact), clamped to [1, 2^64]; h must be
+ * a power of two, so every product here is exact.                            */
+float or_absmax_f32(const float* x, int64_t n, float running, uint32_t* nonfinite);
+float or_absmax_f16(const uint16_t* x, int64_t n, float running, uint32_t* nonfinite);
+float or_scale_from_absmax(float amax, float headroom);
+
 /* ---- loss scaler, [A] §3.4 "Choosing the Loss Scaling Factor" ---- */
 typedef struct {
     float    scale;
