@@ -76,16 +76,42 @@ typedef struct mp_sgd {
     float weight_decay;
 } mp_sgd;
 
+/* Update rules of the sweep (mp_step_opt). The pages name Nesterov-momentum
+ * SGD and Adagrad as the optimizers of their experiments (the analysis page,
+ * §3.1 "Empirical validation (Figure 2a)", §4.5 (Figure 5), §6.4) without
+ * printing the rules; these are the textbook forms:
+ *   MP_OPT_SGD       v = mu v + g;  w = w - lr v
+ *   MP_OPT_NESTEROV  v = mu v + g;  w = w - lr (g + mu v)
+ *   MP_OPT_ADAGRAD   G = G + g g;   w = w - lr (g / (sqrt(G) + eps))
+ * with g = grad16 / S + weight_decay w, one FP32 rounding per operation in
+ * the order written (square root and division correctly rounded). */
+typedef enum { MP_OPT_SGD = 0, MP_OPT_NESTEROV = 1, MP_OPT_ADAGRAD = 2 } mp_opt_kind;
+
+/* Optimizer hyper-parameters, passed by value. momentum is ignored by
+ * Adagrad, eps by the others. */
+typedef struct mp_optim {
+    int32_t kind;              /* mp_opt_kind */
+    float   lr;
+    float   momentum;
+    float   weight_decay;
+    float   eps;               /* Adagrad: > 0 */
+} mp_optim;
+
 /* One parameter tensor of the optimizer sweep (host-side description). */
 typedef struct mp_param {
     float*          master;    /* FP32 master weights [numel], updated in place */
-    float*          momentum;  /* FP32 velocity [numel], updated in place       */
+    float*          momentum;  /* FP32 optimizer state [numel], updated in place:
+                                  the velocity v, or Adagrad's sum G of squares */
     const uint16_t* grad;      /* binary16 loss-scaled gradient [numel], read   */
     uint16_t*       weight16;  /* binary16 working copy [numel], rewritten      */
     int64_t         numel;
 } mp_param;
 
 typedef struct mp_param_list mp_param_list;
+
+/* A list of device tensors of one element type (FP32 or binary16), for the
+ * gradient statistics of loss-scale method 2. */
+typedef struct mp_tensor_list mp_tensor_list;
 
 typedef void* mp_stream;
 
@@ -205,6 +231,16 @@ enum {
 mp_status mp_step(const mp_param_list* list, mp_sgd hyper, mp_scaler* scaler,
                   uint32_t flags, mp_stream stream);
 
+/* The sweep of mp_step with the update rule hyper.kind (see mp_opt_kind):
+ * Steps 5-7 and 1 as for mp_step, the same skip on overflow (nothing written,
+ * Adagrad's sum included), the same check pass and MP_GRADS_PRECHECKED flag.
+ * MP_OPT_SGD gives the bits of mp_step.
+ * Errors: MP_ERR_INVALID_ARGUMENT (list or scaler NULL, unknown kind,
+ * Adagrad with eps not > 0 or not finite), MP_ERR_UNSUPPORTED (unknown flag
+ * bits), MP_ERR_HIP. */
+mp_status mp_step_opt(const mp_param_list* list, mp_optim hyper, mp_scaler* scaler,
+                      uint32_t flags, mp_stream stream);
+
 /* ------------------------------------------------------------------------
  * Loss scaler. Source: the analysis page, §3.4 "Choosing the Loss Scaling
  * Factor": method 1 (constant S, an overflowing step is skipped) and
@@ -224,6 +260,41 @@ mp_status mp_scaler_init(mp_scaler* scaler, float init_scale, int32_t dynamic,
  * doubles (not above 2^64) and count = 0. Then inv_scale = 1/scale and
  * found_inf = 0. One single-lane kernel; no host round trip. */
 mp_status mp_scaler_update(mp_scaler* scaler, mp_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Loss-scale method 2. Source: the analysis page, §3.4 "Choosing the scaling
+ * factor — the direct statistical approach" and the gradient-statistics
+ * recipe after it: record g_max = max |gradient| over all layers during a
+ * short FP32 run, then S = 65504 / g_max, or 65504 / (2 g_max) to leave one
+ * bit of headroom.
+ * ------------------------------------------------------------------------ */
+
+/* Copies n (pointer, length) pairs (host arrays, read during the call) into a
+ * library-owned device table. dtype: MP_F32 or MP_F16 (binary16 bits) for
+ * every tensor. The list remembers pointers, not data.
+ * Errors: MP_ERR_INVALID_ARGUMENT (n < 0, out NULL, null pointer with
+ * numel > 0, numel < 0, other dtype), MP_ERR_OUT_OF_MEMORY, MP_ERR_HIP. */
+mp_status mp_tensor_list_create(const void* const* host_ptrs, const int64_t* host_numel, int32_t n,
+                                mp_dtype dtype, mp_tensor_list** out, mp_stream stream);
+/* Frees the handle after the work queued on its stream at creation (it
+ * synchronises that stream). NULL is accepted. */
+mp_status mp_tensor_list_destroy(mp_tensor_list* list);
+
+/* *amax (device FP32, >= 0 on entry) = max(*amax, |x|) over the finite
+ * elements of every tensor: a running maximum over layers and iterations.
+ * Elements that are +-inf or NaN are left out and, when nonfinite (device
+ * uint32) is not NULL, OR 1 into it. Exact (no rounding is involved).
+ * Errors: MP_ERR_INVALID_ARGUMENT (list or amax NULL), MP_ERR_HIP. */
+mp_status mp_absmax(const mp_tensor_list* list, float* amax, uint32_t* nonfinite, mp_stream stream);
+
+/* Writes a fresh scaler whose scale is the largest power of two S with
+ * S * headroom * (*amax) <= 65504, clamped to [1, 2^64] (a power of two keeps
+ * the unscale exact; headroom 2 is the page's one bit of headroom); count,
+ * found_inf and skipped_steps are 0. amax is read on the device.
+ * headroom must be a power of two in [1, 2^64]; growth_interval >= 1 when
+ * dynamic. Errors: MP_ERR_INVALID_ARGUMENT. */
+mp_status mp_scaler_init_from_absmax(mp_scaler* scaler, const float* amax, float headroom,
+                                     int32_t dynamic, int32_t growth_interval, mp_stream stream);
 
 /* ------------------------------------------------------------------------
  * Auxiliary steps that a full training step needs around the hot path.

@@ -30,6 +30,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mp.h")
 MP_F16, MP_F32 = 0, 1
 MP_GRADS_PRECHECKED = 1
 RELU, GELU = 0, 1
+SGD, NESTEROV, ADAGRAD = 0, 1, 2          # mp_opt_kind
 _STATUS = {0: "MP_OK", 1: "MP_ERR_INVALID_ARGUMENT", 2: "MP_ERR_MISALIGNED",
            3: "MP_ERR_UNSUPPORTED", 4: "MP_ERR_HIP", 5: "MP_ERR_OUT_OF_MEMORY"}
 
@@ -47,6 +48,11 @@ class _Param(C.Structure):
 
 class _Sgd(C.Structure):
     _fields_ = [("lr", C.c_float), ("momentum", C.c_float), ("weight_decay", C.c_float)]
+
+
+class _Optim(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("lr", C.c_float), ("momentum", C.c_float),
+                ("weight_decay", C.c_float), ("eps", C.c_float)]
 
 
 _lib = None
@@ -71,6 +77,11 @@ def lib() -> C.CDLL:
         L.mp_param_list_numel.argtypes = [vp]
         L.mp_param_list_numel.restype = i64
         L.mp_step.argtypes = [vp, _Sgd, vp, u32, vp]
+        L.mp_step_opt.argtypes = [vp, _Optim, vp, u32, vp]
+        L.mp_tensor_list_create.argtypes = [vp, vp, i32, C.c_int, C.POINTER(vp), vp]
+        L.mp_tensor_list_destroy.argtypes = [vp]
+        L.mp_absmax.argtypes = [vp, vp, vp, vp]
+        L.mp_scaler_init_from_absmax.argtypes = [vp, vp, C.c_float, i32, i32, vp]
         L.mp_scaler_init.argtypes = [vp, C.c_float, i32, i32, vp]
         L.mp_scaler_update.argtypes = [vp, vp]
         L.mp_round_f32_to_f16.argtypes = [vp, vp, i64, vp]
@@ -293,6 +304,66 @@ def step(plist: ParamList, scaler: Scaler, lr: float, momentum: float, weight_de
     """One optimizer step over the list (check, then fused update unless overflow)."""
     _check(lib().mp_step(plist.handle, _Sgd(lr, momentum, weight_decay), scaler.ptr, int(flags),
                          _stream(stream)), "mp_step")
+
+
+def step_opt(plist: ParamList, scaler: Scaler, kind: int, lr: float, momentum: float = 0.0,
+             weight_decay: float = 0.0, eps: float = 1e-10, flags: int = 0, stream=None) -> None:
+    """One optimizer step with the update rule `kind` (SGD, NESTEROV or ADAGRAD); for ADAGRAD
+    the list's momentum tensors hold the running sum of squared gradients."""
+    _check(lib().mp_step_opt(plist.handle, _Optim(int(kind), lr, momentum, weight_decay, eps),
+                             scaler.ptr, int(flags), _stream(stream)), "mp_step_opt")
+
+
+# ------------------------------------------------------------------ loss-scale method 2
+class TensorList:
+    """A library-owned table over float32 or binary16 device tensors (gradient statistics)."""
+
+    def __init__(self, tensors, stream=None):
+        n = len(tensors)
+        if n and not all(t.dtype == tensors[0].dtype for t in tensors):
+            raise ValueError("all tensors must have one dtype")
+        dt = tensors[0].dtype if n else torch.float32
+        if dt not in (torch.float32, torch.float16):
+            raise ValueError("float32 or float16 tensors")
+        self._keep = [_dev(t, "tensor", t.element_size()) for t in tensors]
+        for t in self._keep:
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+        ptrs = (C.c_void_p * max(n, 1))(*[t.data_ptr() for t in self._keep])
+        sizes = (C.c_int64 * max(n, 1))(*[t.numel() for t in self._keep])
+        handle = C.c_void_p()
+        _check(lib().mp_tensor_list_create(ptrs, sizes, n, MP_F32 if dt == torch.float32 else MP_F16,
+                                           C.byref(handle), _stream(stream)), "mp_tensor_list_create")
+        self.handle = handle
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            _check(lib().mp_tensor_list_destroy(self.handle), "mp_tensor_list_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def absmax(tlist: TensorList, amax: torch.Tensor, nonfinite: torch.Tensor | None = None, stream=None):
+    """amax (1-element float32 device tensor, >= 0) = max(amax, |x| over the finite elements);
+    nonfinite (1-element int32 device tensor) gets 1 ORed in if any element is +-inf/NaN."""
+    _dev(amax, "amax", 4)
+    nf = None if nonfinite is None else C.c_void_p(_dev(nonfinite, "nonfinite", 4).data_ptr())
+    _check(lib().mp_absmax(tlist.handle, C.c_void_p(amax.data_ptr()), nf, _stream(stream)), "mp_absmax")
+    return amax
+
+
+def scaler_init_from_absmax(scaler: Scaler, amax: torch.Tensor, headroom: float = 2.0,
+                            dynamic: bool = False, growth_interval: int = 2000, stream=None):
+    """Re-initialises `scaler` with S = largest power of two, S * headroom * amax <= 65504."""
+    _check(lib().mp_scaler_init_from_absmax(scaler.ptr, C.c_void_p(_dev(amax, "amax", 4).data_ptr()),
+                                            headroom, int(bool(dynamic)), int(growth_interval),
+                                            _stream(stream)), "mp_scaler_init_from_absmax")
+    return scaler
 
 
 # ------------------------------------------------------------------ auxiliary steps

@@ -4,7 +4,8 @@
 // (paper-graph-ui.vercel.app), §3.4 "The Integrated Training Procedure":
 //   Step 5 unscale the binary16 weight gradients (divide by the loss scale S);
 //   Step 6 if any weight gradient is +-inf or NaN, skip the whole update;
-//   Step 7 SGD with momentum on the FP32 masters, v = mu v + g, w = w - lr v;
+//   Step 7 SGD with momentum on the FP32 masters, v = mu v + g, w = w - lr v
+//   (or, through mp_step_opt, the Nesterov or Adagrad rule of mp_opt_kind);
 //   the weight-decay paragraph: g = g + lambda w with the FP32 master w;
 //   Step 1 the next iteration works on the nearest binary16 copy of w.
 // §3.4 "Choosing the Loss Scaling Factor" gives the constant (method 1) and
@@ -98,20 +99,37 @@ __global__ __launch_bounds__(kThreads) void check_kernel(const DevParam* __restr
 
 // ---------------------------------------------------------------- update pass
 struct Hyper {
-    float lr, mu, wd;
+    float lr, mu, wd, eps;
 };
 
-// One element, in the fixed order of the method (no contraction).
-__device__ __forceinline__ void sgd_elem(float& w, float& v, uint16_t h, float inv, const Hyper& hp,
+// One element, in the fixed order of the method (no contraction). `v` is the
+// optimizer state: the velocity, or Adagrad's sum of squared gradients.
+template <int OPT>
+__device__ __forceinline__ void opt_elem(float& w, float& v, uint16_t h, float inv, const Hyper& hp,
                                          uint16_t& w16) {
     float gs = mp::h2f(h);      // Step 5: binary16 -> FP32 (exact)
     float g = gs * inv;         // Step 5: unscale (exact, power of two)
     float t1 = hp.wd * w;       // weight decay on the FP32 master
     g = g + t1;
-    float t2 = hp.mu * v;       // Step 7: momentum
-    v = t2 + g;
-    float t3 = hp.lr * v;       // Step 7: master update
-    w = w - t3;
+    if (OPT == MP_OPT_ADAGRAD) {
+        float t2 = g * g;       // accumulated squared gradient
+        v = v + t2;
+        float r = sqrtf(v);     // correctly rounded
+        float d = r + hp.eps;
+        float u = g / d;        // correctly rounded
+        float t3 = hp.lr * u;
+        w = w - t3;
+    } else {
+        float t2 = hp.mu * v;   // Step 7: momentum
+        v = t2 + g;
+        float st = v;
+        if (OPT == MP_OPT_NESTEROV) {   // look-ahead step g + mu v
+            float t4 = hp.mu * v;
+            st = g + t4;
+        }
+        float t3 = hp.lr * st;  // Step 7: master update
+        w = w - t3;
+    }
     w16 = mp::f2h(w);           // Step 1: nearest binary16
 }
 
@@ -119,6 +137,7 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
     return uint32_t(lo) | (uint32_t(hi) << 16);
 }
 
+template <int OPT>
 __global__ __launch_bounds__(kThreads) void update_kernel(const DevParam* __restrict__ desc,
                                                           const uint32_t* __restrict__ chunk_tensor,
                                                           const mp_scaler* __restrict__ scaler,
@@ -159,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const DevParam* __rest
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint16_t h = uint16_t(gw[k >> 1] >> ((k & 1) * 16));
-                sgd_elem(wv[k], vv[k], h, inv, hp, hv[k]);
+                opt_elem<OPT>(wv[k], vv[k], h, inv, hp, hv[k]);
             }
             *mp::global(reinterpret_cast<mp::f32x4*>(wp + e)) = mp::f32x4{wv[0], wv[1], wv[2], wv[3]};
             *mp::global(reinterpret_cast<mp::f32x4*>(wp + e + 4)) = mp::f32x4{wv[4], wv[5], wv[6], wv[7]};
@@ -172,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const DevParam* __rest
         for (int e = threadIdx.x; e < len; e += kThreads) {
             float w = wp[e], v = vp[e];
             uint16_t h16;
-            sgd_elem(w, v, gp[e], inv, hp, h16);
+            opt_elem<OPT>(w, v, gp[e], inv, hp, h16);
             wp[e] = w;
             vp[e] = v;
             hp16[e] = h16;
@@ -320,9 +339,10 @@ extern "C" mp_status mp_param_list_destroy(mp_param_list* L) {
 
 extern "C" int64_t mp_param_list_numel(const mp_param_list* L) { return L ? L->numel : 0; }
 
-extern "C" mp_status mp_step(const mp_param_list* L, mp_sgd hyper, mp_scaler* scaler,
-                             uint32_t flags, mp_stream stream) {
-    if (!L || !scaler) return MP_ERR_INVALID_ARGUMENT;
+namespace {
+
+mp_status run_step(const mp_param_list* L, int kind, const Hyper& hp, mp_scaler* scaler,
+                   uint32_t flags, mp_stream stream) {
     if (flags & ~uint32_t(MP_GRADS_PRECHECKED)) return MP_ERR_UNSUPPORTED;
     if (L->chunks == 0) return MP_OK;
     hipStream_t s = mp::as_stream(stream);
@@ -331,9 +351,40 @@ extern "C" mp_status mp_step(const mp_param_list* L, mp_sgd hyper, mp_scaler* sc
         check_kernel<<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, &scaler->found_inf);
         if (mp_status st = mp::launch_status("mp_step/check")) return st;
     }
-    Hyper hp{hyper.lr, hyper.momentum, hyper.weight_decay};
-    update_kernel<<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, scaler, hp, chunks);
+    switch (kind) {
+        case MP_OPT_SGD:
+            update_kernel<MP_OPT_SGD><<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, scaler, hp, chunks);
+            break;
+        case MP_OPT_NESTEROV:
+            update_kernel<MP_OPT_NESTEROV><<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, scaler, hp,
+                                                                      chunks);
+            break;
+        default:
+            update_kernel<MP_OPT_ADAGRAD><<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, scaler, hp,
+                                                                     chunks);
+            break;
+    }
     return mp::launch_status("mp_step/update");
+}
+
+}  // namespace
+
+extern "C" mp_status mp_step(const mp_param_list* L, mp_sgd hyper, mp_scaler* scaler,
+                             uint32_t flags, mp_stream stream) {
+    if (!L || !scaler) return MP_ERR_INVALID_ARGUMENT;
+    const Hyper hp{hyper.lr, hyper.momentum, hyper.weight_decay, 0.0f};
+    return run_step(L, MP_OPT_SGD, hp, scaler, flags, stream);
+}
+
+extern "C" mp_status mp_step_opt(const mp_param_list* L, mp_optim hyper, mp_scaler* scaler,
+                                 uint32_t flags, mp_stream stream) {
+    if (!L || !scaler) return MP_ERR_INVALID_ARGUMENT;
+    if (hyper.kind != MP_OPT_SGD && hyper.kind != MP_OPT_NESTEROV && hyper.kind != MP_OPT_ADAGRAD)
+        return MP_ERR_INVALID_ARGUMENT;
+    if (hyper.kind == MP_OPT_ADAGRAD && !(hyper.eps > 0.0f && hyper.eps <= 3.4028235e38f))
+        return MP_ERR_INVALID_ARGUMENT;
+    const Hyper hp{hyper.lr, hyper.momentum, hyper.weight_decay, hyper.eps};
+    return run_step(L, hyper.kind, hp, scaler, flags, stream);
 }
 
 extern "C" mp_status mp_scaler_init(mp_scaler* scaler, float init_scale, int32_t dynamic,

@@ -37,7 +37,8 @@ def device_asm(name, tmp_path):
 
 
 def kernel_bodies(asm):
-    """{symbol: text} for every kernel entry in the assembly."""
+    """{symbol: text} for every kernel in the assembly, from its label to its .Lfunc_end
+    marker (a kernel can have several s_endpgm, e.g. an early return)."""
     bodies, name, cur = {}, None, []
     for line in asm.splitlines():
         m = re.match(r"^(_Z\w+):", line)
@@ -45,9 +46,10 @@ def kernel_bodies(asm):
             name, cur = m.group(1), []
             bodies[name] = cur
         elif name is not None:
-            cur.append(line)
-            if "s_endpgm" in line:
+            if line.startswith(".Lfunc_end"):
                 name = None
+            else:
+                cur.append(line)
     return {k: "\n".join(v) for k, v in bodies.items()}
 
 
@@ -60,8 +62,17 @@ def test_no_mixed_precision_fma(name, tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 def test_update_kernel_has_no_fused_multiply_add(tmp_path):
+    """The SGD and Nesterov bodies (template kinds 0 and 1) are plain multiplies and adds. The
+    Adagrad body (kind 2) needs a correctly rounded square root and division, whose expansions
+    use fused operations internally; its bits are pinned against the oracle instead, and here it
+    must contain the IEEE division sequence and no mixed-precision FMA."""
     bodies = kernel_bodies(device_asm("mp_step", tmp_path))
-    upd = [v for k, v in bodies.items() if "update_kernel" in k]
-    assert upd, "update kernel not found in the assembly"
-    for body in upd:
-        assert not re.search(r"\bv_(fma|fmac|mad|mac|pk_fma|pk_mul|pk_add)\w*", body)
+    kinds = {k: v for k, v in bodies.items() if "13update_kernel" in k}
+    assert len(kinds) == 3, sorted(kinds)
+    for sym, body in kinds.items():
+        assert "global_load_dwordx4" in body and "global_store_dwordx4" in body, sym   # whole body read
+        if "ILi0E" in sym or "ILi1E" in sym:
+            assert not re.search(r"\bv_(fma|fmac|mad|mac|pk_fma|pk_mul|pk_add)\w*", body), sym
+        else:
+            assert "v_div_fixup_f32" in body and "v_div_fmas_f32" in body, sym
+            assert "v_fma_mix" not in body, sym

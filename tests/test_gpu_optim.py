@@ -1,0 +1,286 @@
+"""GPU parity of the Nesterov and Adagrad sweeps and of loss-scale method 2 (bit-exact).
+
+Sources: "Mixed Precision Training", long-form analysis page: the optimizers of its
+experiments (§3.1 "Empirical validation (Figure 2a)", §4.5 (Figure 5), §6.4), §3.4 "The
+Integrated Training Procedure" (Steps 1, 5-7) and "Choosing the scaling factor — the direct
+statistical approach" (S = 65504 / (2 max|g|)).
+
+Every comparison is bitwise against the oracle: the update rules use one FP32 rounding per
+operation (square root and division correctly rounded on both sides), and a maximum of
+absolute values involves no rounding at all.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_neural_amd as mp
+import oracle
+import workloads
+from gpu_util import (dev_f16, dev_f32, host_bits16, host_f32, require_gpu, same_f16_bits,
+                      same_f32_bits)
+
+pytestmark = pytest.mark.gpu
+
+KINDS = {"nesterov": (mp.NESTEROV, oracle.NESTEROV), "adagrad": (mp.ADAGRAD, oracle.ADAGRAD)}
+
+
+class Run:
+    """The same tensors on the GPU and on the host, stepped by libmp and by the oracle."""
+
+    def __init__(self, ws, vs, gs):
+        self.h_w = [np.array(w, np.float32) for w in ws]
+        self.h_v = [np.array(v, np.float32) for v in vs]
+        self.h_g = [np.array(g, np.uint16) for g in gs]
+        self.h_16 = [oracle.f32_to_f16(w) for w in self.h_w]
+        self.d_w = [dev_f32(w) for w in self.h_w]
+        self.d_v = [dev_f32(v) for v in self.h_v]
+        self.d_g = [dev_f16(g) for g in self.h_g]
+        self.d_16 = [mp.round_f32_to_f16(w) for w in self.d_w]
+
+    def plist(self):
+        return mp.ParamList(self.d_w, self.d_v, self.d_g, self.d_16)
+
+    def set_grads(self, gs):
+        for i, g in enumerate(gs):
+            self.h_g[i][:] = g
+            self.d_g[i].copy_(dev_f16(g))
+
+    def assert_equal(self, what=""):
+        torch.cuda.synchronize()
+        for i in range(len(self.h_w)):
+            assert same_f32_bits(host_f32(self.d_w[i]), self.h_w[i]), f"master {i} {what}"
+            assert same_f32_bits(host_f32(self.d_v[i]), self.h_v[i]), f"state {i} {what}"
+            assert same_f16_bits(host_bits16(self.d_16[i]), self.h_16[i]), f"weight16 {i} {what}"
+
+
+EDGES = np.array([0.0, -0.0, 1.0, -1.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 1.0 - 2 ** -12,
+                  2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25, 1e-40, -1e-40, 65504.0,
+                  65519.0, 65520.0, -65536.0, 1e30, 0.1, -0.3, 123.456], np.float32)
+STATE_EDGES = {"nesterov": EDGES,
+               "adagrad": np.array([0.0, 1e-40, 2.0 ** -126, 1e-20, 1e-6, 0.25, 1.0, 3.0, 1e10, 1e30],
+                                   np.float32)}
+HYPER = {"nesterov": [(0.01, 0.9, 0.0, 0.0), (1e-3, 0.9, 1e-4, 0.0), (2.0 ** -11, 0.0, 0.5, 0.0)],
+         "adagrad": [(0.01, 0.0, 0.0, 1e-10), (1e-3, 0.0, 1e-4, 1e-8), (0.5, 0.0, 0.5, 1.0)]}
+
+
+@pytest.mark.parametrize("name", ["nesterov", "adagrad"])
+@pytest.mark.parametrize("hidx", [0, 1, 2])
+@pytest.mark.parametrize("scale_log2", [0, 10, 24, 64])
+def test_every_finite_f16_gradient_pattern(name, hidx, scale_log2):
+    """Every finite binary16 gradient pattern against edge masters (signed zeros, subnormals,
+    binary16 ties, the overflow boundary) and edge optimizer states."""
+    require_gpu()
+    kd, ko = KINDS[name]
+    lr, mu, wd, eps = HYPER[name][hidx]
+    h = np.arange(1 << 16, dtype=np.uint16)
+    g = h[(h & 0x7C00) != 0x7C00]
+    st = STATE_EDGES[name]
+    n = g.size
+    w = EDGES[np.arange(n) % EDGES.size]
+    v = st[(np.arange(n) // EDGES.size) % st.size]
+    r = Run([w], [v], [g])
+    S = mp.Scaler(2.0 ** scale_log2, True)
+    pl = r.plist()
+    mp.step_opt(pl, S, kd, lr, mu, wd, eps)
+    flag = oracle.step_opt(ko, r.h_w, r.h_v, r.h_g, r.h_16, lr, mu, wd, eps, 2.0 ** -scale_log2)
+    assert flag == 0 and S.read()["found_inf"] == 0
+    r.assert_equal()
+    pl.close()
+
+
+@pytest.mark.parametrize("name", ["nesterov", "adagrad"])
+@pytest.mark.parametrize("bad", [0x7C00, 0xFE01])
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_overflow_skips_every_kind(name, bad, where):
+    """Step 6 for the other rules: nothing is written, Adagrad's sum included; prechecked too."""
+    require_gpu()
+    kd, _ = KINDS[name]
+    rng = np.random.Generator(np.random.PCG64(bad))
+    sizes = [5, 40000, 4097]
+    ws = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    vs = [np.abs(rng.standard_normal(n)).astype(np.float32) for n in sizes]
+    gs = [rng.standard_normal(n).astype(np.float16).view(np.uint16) for n in sizes]
+    gs[1][0 if where == "first" else -1] = bad
+    r = Run(ws, vs, gs)
+    before = ([host_f32(t).copy() for t in r.d_w], [host_f32(t).copy() for t in r.d_v],
+              [host_bits16(t).copy() for t in r.d_16])
+    S = mp.Scaler(1024.0, True)
+    pl = r.plist()
+    mp.step_opt(pl, S, kd, 0.1, 0.9, 0.01, 1e-8)
+    torch.cuda.synchronize()
+    assert S.read()["found_inf"] == 1
+    for i in range(3):
+        assert np.array_equal(host_f32(r.d_w[i]).view(np.uint32), before[0][i].view(np.uint32))
+        assert np.array_equal(host_f32(r.d_v[i]).view(np.uint32), before[1][i].view(np.uint32))
+        assert np.array_equal(host_bits16(r.d_16[i]), before[2][i])
+    pl.close()
+
+
+@pytest.mark.parametrize("name", ["nesterov", "adagrad"])
+@pytest.mark.parametrize("sizes", [[1], [8191, 8192, 8193], [1, 100000, 3, 65536 * 3 + 5]])
+def test_ragged_lists_multi_step(name, sizes):
+    """Five steps over ragged lists (tails shorter than a vector and a chunk) with the dynamic
+    scaler, including an unaligned view (scalar path)."""
+    require_gpu()
+    kd, ko = KINDS[name]
+    rng = np.random.Generator(np.random.PCG64(len(sizes) + 7))
+    ws = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    vs = [np.zeros(n, np.float32) for n in sizes]
+    g_true = [(rng.standard_normal(n) * 2.0 ** -12).astype(np.float32) for n in sizes]
+    gs = [workloads.grads_at_scale(g, 2.0 ** 12) for g in g_true]
+    r = Run(ws, vs, gs)
+    if len(sizes) > 1:                         # make tensor 1 an unaligned view
+        n1 = sizes[1]
+        base = torch.zeros(n1 + 1, dtype=torch.float32, device="cuda")
+        base[1:] = r.d_w[1]
+        r.d_w[1] = base[1:]
+    dS = mp.Scaler(2.0 ** 12, True, 2)
+    oS = oracle.scaler_init(2.0 ** 12, True, 2)
+    pl = r.plist()
+    hp = (1e-3, 0.9, 1e-4, 1e-10)
+    for t in range(5):
+        mp.step_opt(pl, dS, kd, *hp)
+        flag = oracle.step_opt(ko, r.h_w, r.h_v, r.h_g, r.h_16, *hp, oS.inv_scale)
+        dS.update(); oracle.scaler_update(oS, flag)
+        r.assert_equal(f"step {t}")
+        assert dS.read()["scale"] == oS.scale
+        r.set_grads([workloads.grads_at_scale(g, oS.scale) for g in g_true])
+    pl.close()
+
+
+def test_sgd_kind_gives_the_bits_of_mp_step():
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(21))
+    n = 70001
+    w = rng.standard_normal(n).astype(np.float32); v = rng.standard_normal(n).astype(np.float32)
+    g = (rng.standard_normal(n) * 50).astype(np.float16).view(np.uint16)
+    a, b = Run([w], [v], [g]), Run([w], [v], [g])
+    Sa, Sb = mp.Scaler(2.0 ** 6, False), mp.Scaler(2.0 ** 6, False)
+    pa, pb = a.plist(), b.plist()
+    mp.step(pa, Sa, 0.01, 0.9, 1e-4)
+    mp.step_opt(pb, Sb, mp.SGD, 0.01, 0.9, 1e-4)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(a.d_w[0]).view(np.uint32), host_f32(b.d_w[0]).view(np.uint32))
+    assert np.array_equal(host_f32(a.d_v[0]).view(np.uint32), host_f32(b.d_v[0]).view(np.uint32))
+    assert np.array_equal(host_bits16(a.d_16[0]), host_bits16(b.d_16[0]))
+    pa.close(); pb.close()
+
+
+def test_step_opt_argument_errors():
+    require_gpu()
+    r = Run([np.zeros(8, np.float32)], [np.zeros(8, np.float32)], [np.zeros(8, np.uint16)])
+    pl = r.plist()
+    S = mp.Scaler(1.0, False)
+    with pytest.raises(mp.MPError):
+        mp.step_opt(pl, S, 3, 0.1)
+    for eps in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(mp.MPError):
+            mp.step_opt(pl, S, mp.ADAGRAD, 0.1, eps=eps)
+    pl.close()
+
+
+# ---------------------------------------------------------------- loss-scale method 2
+def _ragged(rng, sizes, dtype):
+    out = []
+    for n in sizes:
+        x = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 6, n)).astype(np.float32)
+        out.append(x if dtype == np.float32 else x.astype(np.float16).view(np.uint16))
+    return out
+
+
+def _dev(x):
+    return dev_f32(x) if x.dtype == np.float32 else dev_f16(x)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16])
+@pytest.mark.parametrize("sizes", [[1], [7, 4096, 4097], [100000, 3, 65536 * 3 + 5, 12345]])
+def test_absmax_matches_oracle(dtype, sizes):
+    """Running maximum over ragged lists, including an unaligned view, -0, subnormals and
+    non-finite elements (left out, flagged); a second call keeps the larger running value."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(len(sizes) * 3 + (dtype == np.float32)))
+    xs = _ragged(rng, sizes, dtype)
+    xs[-1][0] = 0x8000 if dtype == np.uint16 else -0.0
+    if len(xs[-1]) > 3:
+        xs[-1][1] = 1 if dtype == np.uint16 else 1e-42
+        xs[-1][2] = 0x7E00 if dtype == np.uint16 else np.nan
+    ds = [_dev(x) for x in xs]
+    if len(ds) > 1:                           # unaligned view of tensor 1
+        base = torch.zeros(ds[1].numel() + 1, dtype=ds[1].dtype, device="cuda")
+        base[1:] = ds[1]
+        ds[1] = base[1:]
+    tl = mp.TensorList(ds)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mp.absmax(tl, amax, nf)
+    ref, ref_bad = oracle.absmax(xs)
+    assert float(amax.item()) == ref and int(nf.item()) == ref_bad
+    # running maximum: a list of small values leaves it unchanged; a larger one raises it
+    small = mp.TensorList([_dev(np.zeros(10, dtype))])
+    mp.absmax(small, amax)
+    assert float(amax.item()) == ref
+    big = np.full(3, 60000.0, np.float32) if dtype == np.float32 else np.full(3, 0x7B53, np.uint16)
+    mp.absmax(mp.TensorList([_dev(big)]), amax)
+    assert float(amax.item()) == oracle.absmax([big], ref)[0]
+    tl.close()
+
+
+@pytest.mark.parametrize("amax", [0.0, 1e-45, 2.0 ** -80, 2.0 ** -10, 0.37, 1.0, 16376.0, 16376.5,
+                                  32752.0, 32753.0, 3e38])
+@pytest.mark.parametrize("headroom", [1.0, 2.0, 8.0])
+def test_scaler_from_absmax_matches_oracle(amax, headroom):
+    require_gpu()
+    S = mp.Scaler(1.0, False)
+    a = torch.tensor([amax], dtype=torch.float32, device="cuda")
+    mp.scaler_init_from_absmax(S, a, headroom, dynamic=True, growth_interval=7)
+    got = S.read()
+    want = oracle.scale_from_absmax(float(np.float32(amax)), headroom)
+    assert got["scale"] == want and got["inv_scale"] == 1.0 / want
+    assert got["count"] == 0 and got["found_inf"] == 0 and got["skipped_steps"] == 0
+    assert got["dynamic"] == 1 and got["growth_interval"] == 7
+
+
+def test_method2_end_to_end_on_c1():
+    """The page's recipe on the two-layer model: FP32 weight gradients of a few iterations ->
+    running max|g| -> S; the same S from the oracle over the same gradients; and a loss-scaled
+    step with that S does not overflow."""
+    require_gpu()
+    cfg = workloads.c1()
+    X = dev_f16(cfg.X16)
+    W16 = [dev_f16(oracle.f32_to_f16(cfg.W1)), dev_f16(oracle.f32_to_f16(cfg.W2))]
+    y = torch.from_numpy(cfg.labels).cuda()
+    Z1 = torch.empty((64, 512), dtype=torch.float16, device="cuda"); H1 = torch.empty_like(Z1)
+    Z2 = torch.empty((64, 10), dtype=torch.float16, device="cuda"); dZ2 = torch.empty_like(Z2)
+    dZ1 = torch.empty_like(Z1)
+    G = [torch.empty(w.shape, dtype=torch.float32, device="cuda") for w in W16]
+    one = mp.Scaler(1.0, False)                  # S = 1: the loss gradient unscaled
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    tl = mp.TensorList(G)
+    host_grads = []
+    for it in range(3):
+        mp.linear_fwd_act(mp.RELU, X, W16[0], Z=Z1, H=H1)
+        mp.linear_fwd(H1, W16[1], Y=Z2)
+        mp.loss_softmax_ce(Z2, y, one, loss, dZ2)
+        mp.linear_wgrad(dZ2, H1, dW=G[1], out_dtype=torch.float32)
+        mp.linear_dgrad_act(mp.RELU, dZ2, W16[1], Z1, dZ=dZ1)
+        mp.linear_wgrad(dZ1, X, dW=G[0], out_dtype=torch.float32)
+        mp.absmax(tl, amax)
+        host_grads += [host_f32(g).copy() for g in G]
+    S = mp.Scaler(1.0, False)
+    mp.scaler_init_from_absmax(S, amax, 2.0)
+    ref_max, _ = oracle.absmax(host_grads)
+    assert float(amax.item()) == ref_max
+    scale = S.read()["scale"]
+    assert scale == oracle.scale_from_absmax(ref_max, 2.0) and scale > 1.0
+    # the scaled binary16 weight gradients of the same iteration stay finite
+    G16 = [torch.empty(w.shape, dtype=torch.float16, device="cuda") for w in W16]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mp.loss_softmax_ce(Z2, y, S, loss, dZ2)
+    mp.linear_wgrad(dZ2, H1, dW=G16[1], found_inf=flag)
+    mp.linear_dgrad_act(mp.RELU, dZ2, W16[1], Z1, dZ=dZ1)
+    mp.linear_wgrad(dZ1, X, dW=G16[0], found_inf=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    assert max(float(g.abs().max()) for g in G16) <= 65504.0 / 2 * 1.01
+    tl.close()
