@@ -58,7 +58,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=32, help="batch rows of the oracle's sample step")
     p.add_argument("--unfused", action="store_true",
                    help="GELU as separate point-wise kernels instead of in the GEMM epilogues")
-    p.add_argument("--pmc-kernel", choices=["fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad", "update", "copy"],
+    p.add_argument("--pmc-kernel", choices=["fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad", "update", "update_nesterov",
+                            "update_adagrad", "absmax", "copy"],
                    help="only launch this kernel --pmc-reps times at the bench's shape (for counter passes)")
     p.add_argument("--pmc-reps", type=int, default=3)
     return p.parse_args()
@@ -96,12 +97,17 @@ def pmc_kernel(args, mp, torch):
              "dgrad": lambda: mp.linear_dgrad(A, B, dX=C),
              "dgrad_act": lambda: mp.linear_dgrad_act(mp.GELU, A, B, D, dZ=C),
              "wgrad": lambda: mp.linear_wgrad(A, B, dW=C, found_inf=flag)}[args.pmc_kernel]
-    elif args.pmc_kernel == "update":
+    elif args.pmc_kernel.startswith("update"):
         N = LAYERS * n * n
         w = torch.randn(N, device="cuda"); v = torch.zeros(N, device="cuda")
         gr = (torch.randn(N, device="cuda") * 1e-3).half(); h = torch.empty(N, device="cuda", dtype=torch.float16)
         S = mp.Scaler(65536.0, True); pl = mp.ParamList([w], [v], [gr], [h])
-        f = lambda: mp.step(pl, S, 0.01, 0.9, 0.0, flags=mp.MP_GRADS_PRECHECKED)
+        kind = {"update": mp.SGD, "update_nesterov": mp.NESTEROV, "update_adagrad": mp.ADAGRAD}[args.pmc_kernel]
+        f = lambda: mp.step_opt(pl, S, kind, 0.01, 0.9, 0.0, 1e-10, flags=mp.MP_GRADS_PRECHECKED)
+    elif args.pmc_kernel == "absmax":
+        x = torch.randn(LAYERS * n * n, device="cuda")
+        tl = mp.TensorList([x]); amax = torch.zeros(1, device="cuda")
+        f = lambda: mp.absmax(tl, amax)
     else:                                   # calibration: 1 GiB read + 1 GiB written per launch
         x = torch.randn(256 * 1024 * 1024, device="cuda"); y = torch.empty_like(x)
         f = lambda: y.copy_(x)
@@ -288,6 +294,40 @@ def main():
     torch.cuda.synchronize()
     two_pass_ms = model.kernel_ms()["sweep2"]["avg_ms"]
 
+    # The other update rules of the sweep (Nesterov, Adagrad) and the method-2
+    # |g| maximum, at the same 201M parameters, on buffers of their own (the
+    # model's masters stay intact): algorithmic 20 B/param for a sweep, 4 B per
+    # FP32 element read for the maximum.
+    variants = {}
+    g_w = [w.clone() for w in model.W]
+    g_s = [torch.zeros_like(w) for w in model.W]
+    g_16 = [torch.empty_like(h) for h in model.W16]
+    vlist = mp.ParamList(g_w, g_s, model.G, g_16)
+    for name, kind in (("nesterov", mp.NESTEROV), ("adagrad", mp.ADAGRAD)):
+        model.events = {}
+        for _ in range(5):
+            model._t(name, mp.step_opt, vlist, model.scaler, kind, lr, mu, wd, 1e-10,
+                     flags=mp.MP_GRADS_PRECHECKED)
+        torch.cuda.synchronize()
+        v_ms = model.kernel_ms()[name]["avg_ms"]
+        gbps = SWEEP_BYTES_PER_PARAM * LAYERS * WIDTH * WIDTH / (v_ms * 1e-3) / 1e9
+        variants[name] = {"avg_us": round(v_ms * 1e3, 2), "achieved_GBps": round(gbps, 1),
+                          "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    vlist.close()
+    tl = mp.TensorList(model.W)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    model.events = {}
+    for _ in range(5):
+        model._t("absmax", mp.absmax, tl, amax)
+    torch.cuda.synchronize()
+    a_ms = model.kernel_ms()["absmax"]["avg_ms"]
+    a_gbps = 4 * LAYERS * WIDTH * WIDTH / (a_ms * 1e-3) / 1e9
+    method2 = {"avg_us": round(a_ms * 1e3, 2), "achieved_GBps": round(a_gbps, 1),
+               "frac": round(a_gbps / PEAK_HBM_GBPS, 4), "bytes": 4 * LAYERS * WIDTH * WIDTH,
+               "input": "FP32, 12 x 4096^2"}
+    tl.close()
+    del g_w, g_s, g_16
+
     gemm_flop = 2.0 * WIDTH * WIDTH * BATCH
     step_flop = gemm_flop * (3 * LAYERS - 1)
     value = step_flop / (ms * 1e-3) / 1e12
@@ -333,6 +373,8 @@ def main():
                     "two_pass_us": round(two_pass_ms * 1e3, 2),
                     "two_pass_GBps": round(SWEEP_BYTES_PER_PARAM * nparam / (two_pass_ms * 1e-3) / 1e9, 1),
                     "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam},
+        "mp_step_opt": variants,
+        "absmax_method2": method2,
         "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")
                    if k in kern},
         "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},

@@ -375,7 +375,7 @@ struct FragAddr {
     }
 };
 
-// The reduction loop for whole 256 x 256 tiles (reduction a multiple of 64,
+// The reduction loop for whole 256 x 256 tiles (reduction a multiple of 128,
 // 16-byte aligned rows, panels under 4 GB). LDS holds two stages per operand:
 // A's at 0 and 32 KB, B's at 64 KB and 96 KB; slab kt lives in stage kt & 1.
 // The loop is unrolled over the two stages, so every LDS address is one of a
@@ -442,7 +442,7 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* lds, 
     auto slab = [&](int kt, auto s_tag, auto next_tag) {
         constexpr int S = decltype(s_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        if constexpr (NEXT) fetch(kt + 1);
+        if constexpr (NEXT) fetch(kt + 1 < nk ? kt + 1 : kt);
         read_frags(S, 0, af[0], bf[0]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -466,18 +466,12 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* lds, 
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using T = std::true_type;
-    using F = std::false_type;
-    int kt = 0;
-    for (; kt + 2 < nk; kt += 2) {                  // steady state: no branches inside
+    // nk is even here. One loop body for every slab: after the last slab the
+    // "next" fetch re-reads that slab into the idle stage (1/nk extra loads),
+    // which keeps the loop free of tail copies the compiler would spill in.
+    for (int kt = 0; kt < nk; kt += 2) {
         slab(kt, C0(), T());
         slab(kt + 1, C1(), T());
-    }
-    // the last 1 or 2 slabs (kt is even here)
-    if (nk - kt == 2) {
-        slab(kt, C0(), T());
-        slab(kt + 1, C1(), F());
-    } else {
-        slab(kt, C0(), F());
     }
 }
 
@@ -696,7 +690,7 @@ mp_status launch_cfg(GemmArgs a, hipStream_t s, const char* name) {
         const int64_t bytes = kc ? (int64_t(BM > BN ? BM : BN) * ld + a.R) * 2 : (a.R + 64) * ld * 2 + 512;
         return bytes < (int64_t(1) << 32);
     };
-    a.pipe_ok = int(panel_ok(A_KC, a.lda) && panel_ok(B_KC, a.ldb));
+    a.pipe_ok = int(panel_ok(A_KC, a.lda) && panel_ok(B_KC, a.ldb) && a.R % (2 * kBK) == 0);
     const uint32_t blocks = uint32_t(a.tiles_m) * uint32_t(a.tiles_n);
     gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, EPI, KIND><<<blocks, 64 * WM * WN, 0, s>>>(a);
     return mp::launch_status(name);
