@@ -304,6 +304,8 @@ def main():
     g_16 = [torch.empty_like(h) for h in model.W16]
     vlist = mp.ParamList(g_w, g_s, model.G, g_16)
     for name, kind in (("nesterov", mp.NESTEROV), ("adagrad", mp.ADAGRAD)):
+        # one untimed call first: it also waits for the list's descriptor upload
+        mp.step_opt(vlist, model.scaler, kind, lr, mu, wd, 1e-10, flags=mp.MP_GRADS_PRECHECKED)
         model.events = {}
         for _ in range(5):
             model._t(name, mp.step_opt, vlist, model.scaler, kind, lr, mu, wd, 1e-10,
@@ -316,6 +318,7 @@ def main():
     vlist.close()
     tl = mp.TensorList(model.W)
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    mp.absmax(tl, amax)                       # untimed: waits for the list's upload
     model.events = {}
     for _ in range(5):
         model._t("absmax", mp.absmax, tl, amax)
