@@ -419,11 +419,14 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* lds, 
         la.store(w8, stage * kAStage);
         lb.store(w8, stage * kBStage);
     };
+    // in the order the MFMAs consume them (A row block 0 with every B block
+    // first), so the first MFMA after a barrier waits for two reads, not five
     auto read_frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = fa.read(l8, i, kk, stage * kAStage);
+        af[0] = fa.read(l8, 0, kk, stage * kAStage);
 #pragma unroll
         for (int j = 0; j < FN; ++j) bf[j] = fb.read(l8, j, kk, stage * kBStage);
+#pragma unroll
+        for (int i = 1; i < FM; ++i) af[i] = fa.read(l8, i, kk, stage * kAStage);
     };
     auto mfma = [&](const half8 (&af)[FM], const half8 (&bf)[FN], int from, int to) {
 #pragma unroll
