@@ -64,14 +64,34 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // ---- point-wise activations on binary16 values (shared by the stand-alone
 // kernels and the fused GEMM epilogues, so both produce the same bits) -------
-// GELU(x) = x * Phi(x) with the exact error function; Phi(x) is evaluated as
-// erfc(-x / sqrt 2) / 2 because 1 + erf(x / sqrt 2) cancels for negative x.
-__device__ __forceinline__ float std_normal_cdf(float x) {
-    return 0.5f * erfcf(-x * 0.70710678118654752440f);
+// GELU(x) = x Phi(x), Phi the standard normal CDF (the exact-erf GELU). For
+// u = |x|, Phi(-u) = e G(u) with e = exp(-u^2/2) and G(u) = Phi(-u) exp(u^2/2)
+// a smooth function; Phi(x) = 1 - Phi(-x) for x >= 0. G is a degree-8
+// polynomial in z = A s + B, s = 1 / (1 + P u), fitted over u in [0, U] (the
+// constants come from gelu_coefficients.py, relative fit error 1e-7; u is
+// clamped to U, where e has made the term negligible). GELU' = Phi(x) + x phi(x)
+// shares e. Both are accurate to a few FP32 ulps, far inside binary16.
+constexpr float kGeluP = 0x1.333334p-2f, kGeluU = 0x1.cp+2f, kGeluA = 0x1.79e79ep+1f, kGeluB = -0x1.f3cf3cp+0f;
+constexpr float kGeluC[9] = {0x1.81feaap-3f, 0x1.97f89cp-3f, 0x1.64adb6p-4f, 0x1.7d75f6p-6f, 0x1.4968e6p-9f, -0x1.d900bp-12f, -0x1.08bb14p-13f, 0x1.208f62p-16f, 0x1.9688d4p-18f};
+struct NormalCdf {
+    float cdf;      // Phi(x)
+    float e;        // exp(-x^2 / 2)
+};
+__device__ __forceinline__ NormalCdf std_normal(float x) {
+    const float u = fminf(fabsf(x), kGeluU);
+    const float e = __expf(-0.5f * (x * x));
+    const float s = __builtin_amdgcn_rcpf(1.0f + kGeluP * u);
+    const float z = __builtin_fmaf(s, kGeluA, kGeluB);
+    float g = kGeluC[8];
+#pragma unroll
+    for (int k = 7; k >= 0; --k) g = __builtin_fmaf(g, z, kGeluC[k]);
+    const float q = e * g;                           // Phi(-|x|)
+    return {x < 0.0f ? q : 1.0f - q, e};
 }
-__device__ __forceinline__ float gelu_f(float x) { return x * std_normal_cdf(x); }
+__device__ __forceinline__ float gelu_f(float x) { return x * std_normal(x).cdf; }
 __device__ __forceinline__ float gelu_d(float x) {
-    return std_normal_cdf(x) + x * 0.39894228040143267794f * expf(-0.5f * x * x);
+    const NormalCdf n = std_normal(x);
+    return n.cdf + (x * 0.39894228040143267794f) * n.e;
 }
 // kind: 0 = ReLU, 1 = GELU (the values of mp_act)
 template <int KIND>
