@@ -186,7 +186,7 @@ __device__ __forceinline__ half8 frag(const uint4* tile, int r0, int kk, int lan
 
 // The reduction loop of one block.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, bool FULL, int FM, int FN>
-__device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64_t row0, int64_t col0,
+__device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* st0, uint4* st1, int64_t row0, int64_t col0,
                                             int tid, int lane, int wm, int wn,
                                             floatx16 (&acc)[FM][FN]) {
     constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -198,8 +198,8 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
     if (nk <= 0) return;
     la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, 0, tid);
     lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, 0, tid);
-    la.store(lds, tid);
-    lb.store(lds + BM * kRowChunks, tid);
+    la.store(st0, tid);
+    lb.store(st0 + BM * kRowChunks, tid);
     __syncthreads();
 
     auto read_frags = [&](const uint4* st, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
@@ -235,8 +235,8 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
             const int64_t k0 = int64_t(kt + 1) * kBK;
             la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, k0, tid);
             lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, k0, tid);
-            slice(lds + cur * kStage);
-            uint4* nxt = lds + (cur ^ 1) * kStage;
+            slice(cur ? st1 : st0);
+            uint4* nxt = cur ? st0 : st1;
             la.store(nxt, tid);
             lb.store(nxt + BM * kRowChunks, tid);
             // Instruction order of the slice (groups are filled in program order).
@@ -261,9 +261,9 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
             la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, k0, tid);
             lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, k0, tid);
         }
-        slice(lds + cur * kStage);
+        slice(cur ? st1 : st0);
         if (more) {
-            uint4* nxt = lds + (cur ^ 1) * kStage;
+            uint4* nxt = cur ? st0 : st1;
             la.store(nxt, tid);
             lb.store(nxt + BM * kRowChunks, tid);
         }
@@ -271,52 +271,48 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* lds, int64
     }
 }
 
-// One operand's slab (ROWS index rows x 64 reduction elements) fetched with
-// buffer loads: a resource over the operand's panel in scalar registers, a
-// fixed 32-bit byte offset per chunk in a vector register, and a scalar offset
-// per slab, so the loop does no vector address arithmetic. Chunk u of a thread
-// is the TileLoader's chunk tid + 256 u; its LDS address is one of two
-// per-lane values (KC: the swizzle of rows 32 apart differs in bit 2) plus
-// the immediate 4096 u.
-template <int ROWS, int NT, bool KC>
-struct PipeLoader {
-    static constexpr int kPer = ROWS * kRowChunks / NT;
+// One operand's slab (ROWS index rows x 64 reduction elements) fetched by
+// buffer loads that write LDS directly: lane i of such a load stores its 16
+// bytes at the instruction's LDS address + 16 i, so each wave fills kPer whole
+// 1 KB blocks of the operand's region, and lane i of block b fetches the global
+// chunk that the fragment layout places at chunk 64 b + i (both swizzles are
+// XORs, hence their own inverses). No registers hold the slab and no LDS store
+// instructions are issued. The resource covers the operand's panel; each lane
+// keeps a fixed 32-bit byte offset per block, and the slab is a scalar offset.
+template <int ROWS, int WAVES, bool KC>
+struct DmaLoader {
+    static constexpr int kBlocks = ROWS * kRowChunks / 64;   // 1 KB blocks per slab
+    static constexpr int kPer = kBlocks / WAVES;
     static constexpr int C = ROWS / 8;                       // 16-byte chunks per MN row
-    static_assert(NT == 256 && ROWS == 256, "chunk u of a thread is 32 KC rows / 8 MN rows further");
+    static_assert(kBlocks % WAVES == 0, "the waves share the blocks evenly");
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t voff[kPer];
-    uint32_t lds0, lds1;
-    mp::u32x4 r[kPer];
+    uint32_t blk0;                                           // wave's first block, bytes (uniform)
 
-    // panel: A(row0, 0) for KC, A(0, row0) for MN; lds_base: byte offset of the operand's stage 0
-    __device__ __forceinline__ void init(const uint16_t* panel, int64_t ld, int tid, uint32_t lds_base) {
+    // panel: A(row0, 0) for KC, A(0, row0) for MN; wave: a wave-uniform index
+    __device__ __forceinline__ void init(const uint16_t* panel, int64_t ld, int wave, int lane) {
         rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(panel), 0, -1, 0x00020000);
+        blk0 = uint32_t(wave * kPer * 1024);
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int q = tid + u * NT;
-            if (KC) voff[u] = uint32_t(((q / kRowChunks) * ld + (q % kRowChunks) * 8) * 2);
-            else voff[u] = uint32_t(((q / C) * ld + (q % C) * 8) * 2);
-        }
-        if (KC) {
-            const int row = tid / kRowChunks, kc = tid % kRowChunks;
-            lds0 = lds_base + uint32_t(row * 128 + 16 * (kc ^ swz_kc(row)));
-            lds1 = lds_base + uint32_t(row * 128 + 16 * (kc ^ swz_kc(row) ^ 4));
-        } else {
-            const int k = tid / C, cb = tid % C;
-            lds0 = lds1 = lds_base + uint32_t((k * C + (cb ^ swz_mn<C>(k))) * 16);
+        for (int t = 0; t < kPer; ++t) {
+            const int q = (wave * kPer + t) * 64 + lane;         // LDS chunk this lane fills
+            if (KC) {
+                const int row = q / kRowChunks, kc = (q % kRowChunks) ^ swz_kc(row);
+                voff[t] = uint32_t((int64_t(row) * ld + kc * 8) * 2);
+            } else {
+                const int k = q / C, cb = (q % C) ^ swz_mn<C>(k);
+                voff[t] = uint32_t((int64_t(k) * ld + cb * 8) * 2);
+            }
         }
     }
-    // soff: byte offset of the slab within the panel
-    __device__ __forceinline__ void fetch(uint32_t soff) {
+    // region: the operand's part of the target stage; soff: the slab's byte offset in the panel
+    __device__ __forceinline__ void fetch(__attribute__((address_space(3))) uint8_t* region, uint32_t soff) const {
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-        for (int u = 0; u < kPer; ++u)
-            r[u] = __builtin_bit_cast(mp::u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[u], soff, 0));
-    }
-    __device__ __forceinline__ void store(__attribute__((address_space(3))) uint8_t* lds, uint32_t stage_off) const {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u)
-            *reinterpret_cast<__attribute__((address_space(3))) mp::u32x4*>(
-                lds + ((u & 1) ? lds1 : lds0) + 4096 * u + stage_off) = r[u];
+        for (int t = 0; t < kPer; ++t)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(region + blk0 + t * 1024), 16, voff[t], soff, 0, 0);
+#endif
     }
 };
 
@@ -376,113 +372,106 @@ struct FragAddr {
 };
 
 // The reduction loop for whole 256 x 256 tiles (reduction a multiple of 128,
-// 16-byte aligned rows, panels under 4 GB). LDS holds two stages per operand:
-// A's at 0 and 32 KB, B's at 64 KB and 96 KB; slab kt lives in stage kt & 1.
-// The loop is unrolled over the two stages, so every LDS address is one of a
-// few per-lane registers plus an immediate, and the loads are buffer loads
-// with a scalar slab offset: no vector address arithmetic per slab. Each slab
-// fetches the next one into registers under its first sub-step and stores it
-// into the other stage under its last, then a barrier.
+// 16-byte aligned rows, panels under 4 GB). Stage s is the LDS variable st[s]
+// (A's slab at byte 0, B's at kAStage); slab kt lives in stage kt & 1. The two
+// stages are separate variables so that the compiler can tell a fragment read
+// of one stage from a load in flight into the other and waits for those loads
+// only where this code says so. The loop is unrolled over the two stages, so
+// every LDS address is one of a few per-lane registers plus an immediate. Each
+// slab issues the next slab's loads into the other stage under its first two
+// sub-steps, waits for them at its end, then a barrier.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int FM, int FN>
-__device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* lds, int64_t row0, int64_t col0,
-                                                 int tid, int lane, int wm, int wn, floatx16 (&acc)[FM][FN]) {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
+__device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, uint4* st1, int64_t row0,
+                                                 int64_t col0, int lane, int wm, int wn,
+                                                 floatx16 (&acc)[FM][FN]) {
+    constexpr int WAVES = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    constexpr uint32_t kAStage = BM * kRowChunks * 16, kBStage = BN * kRowChunks * 16;   // bytes
-    constexpr uint32_t kBBase = 2 * kAStage;
+    constexpr uint32_t kAStage = BM * kRowChunks * 16;                    // bytes
     constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per sub-step
-    using LA = PipeLoader<BM, NT, A_KC>;
-    using LB = PipeLoader<BN, NT, B_KC>;
-    constexpr int kLoads = LA::kPer + LB::kPer;                          // loads / stores per thread
+    using LA = DmaLoader<BM, WAVES, A_KC>;
+    using LB = DmaLoader<BN, WAVES, B_KC>;
+    constexpr int kLoads = LA::kPer + LB::kPer;                          // loads per wave per slab
     static_assert(FM == 4 && FN == 4 && WTM == 128 && WTN == 128, "4 x 4 blocks of 32 x 32 per wave");
-    static_assert(kReads <= 16 && kLoads <= 16, "one sub-step = 16 MFMAs");
-    static_assert(kAStage <= 32768 && kBStage <= 32768, "stage offsets must fit the LDS immediate");
+    static_assert(kReads <= 16 && kLoads <= 32, "one sub-step = 16 MFMAs");
+    static_assert(kAStage <= 32768 && BN * kRowChunks * 16 <= 32768, "fragment offsets must fit the LDS immediate");
     const int nk = int(g.R / kBK);
-    lds_u8* l8 = (lds_u8*)(lds);
-    __attribute__((address_space(3))) uint8_t* w8 = (__attribute__((address_space(3))) uint8_t*)(lds);
+    typedef __attribute__((address_space(3))) uint8_t lds8;
+    lds8* s8[2] = {(lds8*)st0, (lds8*)st1};
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     LA la;
     LB lb;
-    la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, tid, 0);
-    lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, tid, kBBase);
+    la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, wave, lane);
+    lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, wave, lane);
     FragAddr<BM, A_KC> fa;
     FragAddr<BN, B_KC> fb;
     fa.init(wm * WTM, lane, 0);
-    fb.init(wn * WTN, lane, kBBase);
+    fb.init(wn * WTN, lane, kAStage);
     // byte offset of slab kt within a panel: 64 elements along a KC row, 64 rows of an MN panel
     const uint32_t a_step = A_KC ? 2 * kBK : uint32_t(2 * kBK * g.lda);
     const uint32_t b_step = B_KC ? 2 * kBK : uint32_t(2 * kBK * g.ldb);
-    auto fetch = [&](int kt) {
-        la.fetch(uint32_t(kt) * a_step);
-        lb.fetch(uint32_t(kt) * b_step);
-    };
-    auto store = [&](int stage) {
-        la.store(w8, stage * kAStage);
-        lb.store(w8, stage * kBStage);
+    auto fetch = [&](int kt, int stage) {
+        la.fetch(s8[stage], uint32_t(kt) * a_step);
+        lb.fetch(s8[stage] + kAStage, uint32_t(kt) * b_step);
     };
     // in the order the MFMAs consume them (A row block 0 with every B block
     // first), so the first MFMA after a barrier waits for two reads, not five
     auto read_frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
-        af[0] = fa.read(l8, 0, kk, stage * kAStage);
+        af[0] = fa.read(s8[stage], 0, kk, 0);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[j] = fb.read(l8, j, kk, stage * kBStage);
+        for (int j = 0; j < FN; ++j) bf[j] = fb.read(s8[stage], j, kk, 0);
 #pragma unroll
-        for (int i = 1; i < FM; ++i) af[i] = fa.read(l8, i, kk, stage * kAStage);
+        for (int i = 1; i < FM; ++i) af[i] = fa.read(s8[stage], i, kk, 0);
     };
     auto mfma = [&](const half8 (&af)[FM], const half8 (&bf)[FN], int from, int to) {
 #pragma unroll
         for (int t = from; t < to; ++t)
             acc[t / FN][t % FN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[t % FN], af[t / FN], acc[t / FN][t % FN], 0, 0, 0);
     };
+    // vmcnt(0), expcnt and lgkmcnt left at their maxima: this wave's loads into LDS have landed
+    auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     half8 af[2][FM], bf[2][FN];
     // Prologue: slab 0 in stage 0.
-    fetch(0);
-    store(0);
+    fetch(0, 0);
+    wait_loads();
     __syncthreads();
 
-    // One slab in stage S; NEXT: slab kt + 1 exists, is fetched under the first
-    // two sub-steps and stored into the other stage under the last two.
-    auto slab = [&](int kt, auto s_tag, auto next_tag) {
+    // One slab in stage S; the next slab (or, after the last, a copy of it) is
+    // loaded into the other stage.
+    auto slab = [&](int kt, auto s_tag) {
         constexpr int S = decltype(s_tag)::value;
-        constexpr bool NEXT = decltype(next_tag)::value;
-        if constexpr (NEXT) fetch(kt + 1 < nk ? kt + 1 : kt);
+        fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
         read_frags(S, 0, af[0], bf[0]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if (kk < 3) read_frags(S, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
             mfma(af[kk & 1], bf[kk & 1], 0, 16);
         }
-        if constexpr (NEXT) store(S ^ 1);
         // Instruction order (groups are filled in program order): the first
         // fragments, then each MFMA followed by the next sub-step's fragment
-        // reads (sub-steps 0-2), a global load after every other MFMA of
-        // sub-steps 0 and 1, and a store of the next slab after every other
-        // MFMA of sub-steps 2 and 3. Four waves issuing their 16 loads within
-        // one sub-step ask the CU's vector-memory path for about twice what it
-        // moves per cycle, and the waiting issue holds up the MFMAs; spread
-        // over two sub-steps the loads were ~4% faster at 4096^3, and the
-        // stores spread likewise ~2%.
+        // reads (sub-steps 0-2) and, after every other MFMA of sub-steps 0
+        // and 1, a load of the next slab. Four waves issuing all their loads
+        // within one sub-step ask the CU's vector-memory path for about twice
+        // what it moves per cycle, and the waiting issue holds up the MFMAs.
         __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
         for (int kk = 0; kk < 4; ++kk)
             for (int m = 0; m < 16; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (NEXT && kk < 2 && !(m & 1) && kk * 8 + m / 2 < kLoads)
+                if (kk < 2 && !(m & 1) && kk * 8 + m / 2 < kLoads)
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 if (kk < 3 && m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (NEXT && kk >= 2 && (m & 1) && (kk - 2) * 8 + m / 2 < kLoads)
-                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
+        wait_loads();
         __syncthreads();
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    using T = std::true_type;
     // nk is even here. One loop body for every slab: after the last slab the
-    // "next" fetch re-reads that slab into the idle stage (1/nk extra loads),
-    // which keeps the loop free of tail copies the compiler would spill in.
+    // "next" load re-reads that slab into the idle stage (1/nk extra loads),
+    // which keeps the loop free of tail copies.
     for (int kt = 0; kt < nk; kt += 2) {
-        slab(kt, C0(), T());
-        slab(kt + 1, C1(), T());
+        slab(kt, C0());
+        slab(kt + 1, C1());
     }
 }
 
@@ -505,7 +494,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int kStage = (BM + BN) * kRowChunks;         // uint4 per LDS stage
-    __shared__ uint4 lds[2 * kStage];
+    // the two stages of the reduction loop, as two variables (see reduce_tile_pipe)
+    __shared__ uint4 lds0[kStage];
+    __shared__ uint4 lds1[kStage];
     static_assert(BM % 32 == 0 && BN % 32 == 0, "tile must be whole MFMA tiles");
 
     const int tid = threadIdx.x;
@@ -538,16 +529,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
     bool done = false;
     if constexpr (BM == 256 && BN == 256) {
         if (full && g.pipe_ok) {
-            reduce_tile_pipe<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, FM, FN>(g, lds, row0, col0, tid, lane, wm, wn, acc);
+            reduce_tile_pipe<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, FM, FN>(g, lds0, lds1, row0, col0, lane, wm, wn, acc);
             done = true;
         }
     }
     if (done) {
     } else if (full)
-        reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, true, FM, FN>(g, lds, row0, col0, tid, lane,
+        reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, true, FM, FN>(g, lds0, lds1, row0, col0, tid, lane,
                                                                       wm, wn, acc);
     else
-        reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, false, FM, FN>(g, lds, row0, col0, tid, lane,
+        reduce_tile<BM, BN, WAVES_M, WAVES_N, A_KC, B_KC, false, FM, FN>(g, lds0, lds1, row0, col0, tid, lane,
                                                                        wm, wn, acc);
 
     // ---- epilogue. The MFMA takes B's fragment as its first operand, so the
@@ -585,10 +576,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
     // then reads it back a 16-byte row piece per lane and stores whole rows.
     constexpr int kChunks = WTN / 8;                     // 16-byte chunks per staged row
     constexpr int kRowsPerPass = 64 / kChunks;
-    static_assert(WTM * WTN * 2 * WAVES_M * WAVES_N <= 2 * kStage * 16, "staged tile must fit in LDS");
     static_assert(WTM % kRowsPerPass == 0, "whole passes");
     uint32_t bad = 0;
-    uint8_t* stage = reinterpret_cast<uint8_t*>(lds) + size_t(wave) * WTM * WTN * 2;
+    constexpr int kWaveBytes = WTM * WTN * 2, kFit0 = kStage * 16 / kWaveBytes;
+    static_assert(WAVES_M * WAVES_N <= 2 * kFit0, "each wave's staged tile lies within one stage");
+    uint8_t* stage = wave < kFit0 ? reinterpret_cast<uint8_t*>(lds0) + size_t(wave) * kWaveBytes
+                                  : reinterpret_cast<uint8_t*>(lds1) + size_t(wave - kFit0) * kWaveBytes;
     uint16_t* C = static_cast<uint16_t*>(g.C);
     // Whole wave tiles with 16-byte access everywhere take an unchecked path.
     const bool whole = g.c_vec && (EPI == kEpiF16 || g.aux_vec) && wrow0 + WTM <= g.Mc &&
