@@ -39,7 +39,7 @@ CHECK_BYTES_PER_PARAM = 2
 # fetch figure is scaled by 2.0 and the write figure by 1.0. A figure holds only for the kernel
 # source it was taken on: it is reported while the SHA-256 of those files still matches.
 MEASURED_TRAFFIC = {
-    "gemm": {"src": ["mp_gemm.hip", "mp_internal.h"],
+    "gemm": {"src": ["mp_gemm.hip", "mp_internal.h", "mp_act.h"],
              "sha256": "fc0cd1eaa7cb1d827f4448616a8a3f8ee3773a5a77185c80a2b0fd9bb02bf685",
              "fwd": (98571.1, 33536.0), "fwd_act": (98511.5, 66048.0), "dgrad_act": (114917.7, 32768.0),
              "wgrad": (98660.9, 33280.0)},

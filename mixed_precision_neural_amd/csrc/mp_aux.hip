@@ -13,7 +13,7 @@
 // single block), so the loss value is deterministic; the loss gradient is
 // S * dL/dy in FP32, rounded once to binary16. S is read from the device
 // scaler, so no host round trip is needed.
-#include "mp_internal.h"
+#include "mp_act.h"
 
 namespace {
 

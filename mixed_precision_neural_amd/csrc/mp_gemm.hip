@@ -41,7 +41,7 @@
 // own L2. Binary16 outputs are rounded into LDS and written back as whole
 // 16-byte row pieces; the activation-fused modes apply the point-wise step to
 // those pieces.
-#include "mp_internal.h"
+#include "mp_act.h"
 
 #include <type_traits>
 
