@@ -122,6 +122,19 @@ def test_fused_c4_layer_shape():
     check_dgrad(mp.GELU, dY, W, Zs, dYd, Wd, Zd, ref=False)
 
 
+def test_fused_direct_to_lds_ragged():
+    """Ragged grids of 256 x 256 tiles whose whole tiles take the direct-to-LDS loop and whose
+    edge tiles take the general loop, in both fused layers (forward 17 x 17 tiles, K = 2176;
+    dgrad 17 x 9 tiles, reduction 4352): bitwise equal to the unfused pair, the activation
+    checked against the oracle on every output."""
+    require_gpu()
+    M, N, K = 4100, 4352, 2176
+    X, W, dY, Zs = inputs(M, N, K, 4352)
+    Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
+    check_fwd(mp.GELU, X, W, Xd, Wd, ref=False)
+    check_dgrad(mp.GELU, dY, W, Zs, dYd, Wd, Zd, ref=False)
+
+
 def test_fused_argument_errors():
     require_gpu()
     a = torch.zeros((8, 8), dtype=torch.float16, device="cuda")

@@ -42,8 +42,9 @@ def gpu_all(X, W, dY, out=torch.float32):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (64, 10, 32), (17, 300, 24), (300, 257, 32),
                                    (2600, 3100, 32), (512, 768, 256), (1024, 512, 1536)])
 def test_exact_integer_sums(M, N, K):
-    """Shapes whose tiles are all whole (multiples of 256, reductions multiples of 128) take the
-    direct-to-LDS kernel; the others the general kernel.
+    """Grids of fewer than 128 tiles of 256 x 256 run the 64 x 64 kernel; the others the 256 x
+    256 kernel's general loop here (reductions that are not multiples of 128). The direct-to-LDS
+    loop is pinned the same way by test_exact_integer_sums_direct_to_lds.
 
     Pin P8: on a 2^-q grid with |x| <= 2 every product is a multiple of 2^-2q below 4, so a
     partial sum over R terms is a multiple of 2^-2q below 4R: exact in FP32 while 4R * 2^2q <= 2^24.
@@ -88,6 +89,28 @@ def test_fp32_accumulation_discriminator():
     W = rng.standard_normal((192, K)).astype(np.float16).view(np.uint16)
     got = host_f32(mp.linear_fwd(dev_f16(X), dev_f16(W), out_dtype=torch.float32))
     assert rel_err(got, oracle.linear_fwd(X, W)) <= TOL_F32
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 2048), (4100, 4352, 2176), (2048, 8192, 128)])
+def test_exact_integer_sums_direct_to_lds(M, N, K):
+    """Pin P8 on the 256 x 256 kernel's direct-to-LDS loop (128 or more big tiles; whole tiles,
+    reductions multiples of 128): 4096 x 4096 x 2048 sends all three layers through it;
+    4100 x 4352 x 2176 mixes whole tiles with ragged edge tiles (general loop) in one launch, and
+    its wgrad reduction (4100) is not a multiple of 128; 2048 x 8192 x 128 is the two-slab minimum
+    for the forward layer. Integer sums below 2^53 are exact in float64, so the reference is a
+    float64 product of the integer grids."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(M + 2 * N + 3 * K))
+    q = 4
+    assert 4 * max(M, N, K) * 2 ** (2 * q) <= 2 ** 24
+    X, Xi = grid_bits(rng, (M, K), -q); W, Wi = grid_bits(rng, (N, K), -q)
+    dY, dYi = grid_bits(rng, (M, N), -q)
+    y, dx, dw = gpu_all(X, W, dY)
+    Xf, Wf, dYf = Xi.astype(np.float64), Wi.astype(np.float64), dYi.astype(np.float64)
+    q2 = 2.0 ** (-2 * q)
+    assert np.array_equal(y.astype(np.float64), (Xf @ Wf.T) * q2)
+    assert np.array_equal(dx.astype(np.float64), (dYf @ Wf) * q2)
+    assert np.array_equal(dw.astype(np.float64), (dYf.T @ Xf) * q2)
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 512, 256), (64, 10, 512), (300, 520, 200), (777, 1000, 333),
