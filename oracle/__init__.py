@@ -92,6 +92,9 @@ def lib():
         L.or_mse.argtypes = [u16p, u16p, i64, i64, C.c_double, C.c_double, u16p]
         L.or_mse.restype = C.c_double
         L.or_mse_grad_f64.argtypes = [u16p, u16p, i64, i64, i64, C.c_double, vp]
+        L.or_bn_stats.argtypes = [u16p, i64, i64, i64, vp, vp]
+        L.or_bn_apply.argtypes = [u16p, i64, i64, i64, vp, vp, vp, vp, C.c_float, u16p, i64]
+        L.or_softmax.argtypes = [u16p, i64, i64, i64, u16p, i64]
         L.or_set_threads.argtypes = [i32]
         L.or_get_threads.restype = i32
         _lib = L
@@ -322,3 +325,46 @@ def mse_grad_f64(y, t, m_total, c):
     d = np.empty((M, N), np.float64)
     lib().or_mse_grad_f64(_p(y), _p(t), M, N, int(m_total), float(c), _p(d))
     return d
+
+
+# ---------------------------------------------------------------- large reductions
+# [A] §3.4 "FP16 Arithmetic with FP32 Accumulation": batch-normalization statistics and
+# softmax sums are large reductions done in FP32 from binary16 tensors, and the
+# normalization arithmetic is FP32.
+def _rows(a) -> tuple:
+    """(array, rows, cols, row pitch in elements) of a 2-D uint16 array whose rows are
+    contiguous; a row-strided view is passed as it is."""
+    a = np.asarray(a)
+    if a.dtype != np.uint16 or a.ndim != 2:
+        raise TypeError("expected a 2-D uint16 array")
+    if a.strides[1] != 2 or a.strides[0] % 2 or a.strides[0] < 2 * a.shape[1]:
+        a = np.ascontiguousarray(a)
+    ld = a.strides[0] // 2 if a.shape[0] > 1 else a.shape[1]
+    return a, a.shape[0], a.shape[1], max(ld, a.shape[1])
+
+
+def bn_stats(x):
+    """Per-channel (mean, population variance) in float64 over the rows of x[rows, C]."""
+    x, rows, cols, ld = _rows(x)
+    mean = np.empty(cols, np.float64); var = np.empty(cols, np.float64)
+    lib().or_bn_stats(_p(x), rows, cols, ld, _p(mean), _p(var))
+    return mean, var
+
+
+def bn_apply(x, mean, var, gamma, beta, eps):
+    """y = RNE16(((x - mean) * (1 / sqrt(var + eps))) * gamma + beta) in FP32, in that order."""
+    x, rows, cols, ld = _rows(x)
+    f = [np.ascontiguousarray(a, np.float32) for a in (mean, var, gamma, beta)]
+    if any(a.shape != (cols,) for a in f):
+        raise ValueError("per-channel arrays must have one value per column")
+    y = np.empty((rows, cols), np.uint16)
+    lib().or_bn_apply(_p(x), rows, cols, ld, *[_p(a) for a in f], float(eps), _p(y), cols)
+    return y
+
+
+def softmax(x):
+    """Row-wise softmax of x[rows, cols] in float64, rounded once to binary16."""
+    x, rows, cols, ld = _rows(x)
+    y = np.empty((rows, cols), np.uint16)
+    lib().or_softmax(_p(x), rows, cols, ld, _p(y), cols)
+    return y

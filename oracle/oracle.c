@@ -573,3 +573,66 @@ void or_mse_grad_f64(const uint16_t* y, const uint16_t* t, int64_t M_rows, int64
         dy[i] = c * 2.0 * d / mn;
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Large reductions ([A] §3.4 "FP16 Arithmetic with FP32 Accumulation": batch-  */
+/* normalization statistics and softmax sums are summed in FP32 from binary16   */
+/* tensors, and the normalization arithmetic is FP32).                         */
+/* ------------------------------------------------------------------------- */
+
+void or_bn_stats(const uint16_t* x, int64_t rows, int64_t C, int64_t ldx, double* mean, double* var) {
+    for (int64_t c = 0; c < C; ++c) { mean[c] = 0.0; var[c] = 0.0; }
+    if (rows <= 0) return;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < C; ++c) mean[c] += (double)or_f16_to_f32(x[r * ldx + c]);
+    for (int64_t c = 0; c < C; ++c) mean[c] /= (double)rows;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            double d = (double)or_f16_to_f32(x[r * ldx + c]) - mean[c];
+            var[c] += d * d;
+        }
+    for (int64_t c = 0; c < C; ++c) var[c] /= (double)rows;
+}
+
+void or_bn_apply(const uint16_t* x, int64_t rows, int64_t C, int64_t ldx, const float* mean,
+                 const float* var, const float* gamma, const float* beta, float eps,
+                 uint16_t* y, int64_t ldy) {
+    for (int64_t c = 0; c < C; ++c) {
+        float s = var[c] + eps;
+        float r = sqrtf(s);
+        float inv = 1.0f / r;
+        for (int64_t i = 0; i < rows; ++i) {
+            float t = or_f16_to_f32(x[i * ldx + c]) - mean[c];
+            float u = t * inv;
+            float v = u * gamma[c];
+            float w = v + beta[c];
+            y[i * ldy + c] = or_f32_to_f16(w);
+        }
+    }
+}
+
+typedef struct { const uint16_t* x; uint16_t* y; int64_t cols, ldx, ldy; } sm_ctx;
+
+static void softmax_rows(int64_t lo, int64_t hi, void* p) {
+    sm_ctx* c = (sm_ctx*)p;
+    for (int64_t r = lo; r < hi; ++r) {
+        const uint16_t* xr = c->x + r * c->ldx;
+        uint16_t* yr = c->y + r * c->ldy;
+        double m = -INFINITY;
+        int bad = 0;
+        for (int64_t j = 0; j < c->cols; ++j) {
+            double v = (double)or_f16_to_f32(xr[j]);
+            if (isnan(v) || v == INFINITY) bad = 1;
+            if (v > m) m = v;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < c->cols; ++j) s += exp((double)or_f16_to_f32(xr[j]) - m);
+        for (int64_t j = 0; j < c->cols; ++j)
+            yr[j] = bad ? d_to_f16(NAN) : d_to_f16(exp((double)or_f16_to_f32(xr[j]) - m) / s);
+    }
+}
+
+void or_softmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy) {
+    sm_ctx c = {x, y, cols, ldx, ldy};
+    parallel_for(rows, 1, softmax_rows, &c);
+}

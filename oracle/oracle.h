@@ -134,6 +134,26 @@ double or_mse(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N, double
 void or_mse_grad_f64(const uint16_t* y, const uint16_t* t, int64_t M_rows, int64_t N,
                      int64_t M_total, double c, double* dy);
 
+/* ---- large reductions, [A] §3.4 "FP16 Arithmetic with FP32 Accumulation" (large
+ * reductions: batch-normalization statistics and softmax sums in FP32 from binary16
+ * tensors). The statistics and the softmax are evaluated in double (their exact
+ * values, to which a device's FP32 reductions in any order are compared within a
+ * bound); the normalization is element-wise, so it follows the pages' FP32 with one
+ * rounding per operation in a fixed order.                                       */
+/* Per-channel mean and population variance over the rows of x[rows, C] (row pitch
+ * ldx elements): mean = sum(x) / rows, var = sum((x - mean)^2) / rows (two passes). */
+void or_bn_stats(const uint16_t* x, int64_t rows, int64_t C, int64_t ldx, double* mean, double* var);
+/* y = RNE16(w) with, per channel c, s = var + eps, r = sqrt(s), inv = 1 / r, and per
+ * element t = x - mean, u = t * inv, v = u * gamma, w = v + beta: FP32, one rounding
+ * per operation, in this order.                                                 */
+void or_bn_apply(const uint16_t* x, int64_t rows, int64_t C, int64_t ldx, const float* mean,
+                 const float* var, const float* gamma, const float* beta, float eps,
+                 uint16_t* y, int64_t ldy);
+/* Row-wise softmax of x[rows, cols]: y = RNE16(exp(x - m) / sum exp(x - m)), m the row
+ * maximum, in double. A row with a NaN or +inf gives NaN throughout; -inf gives 0
+ * (a row of only -inf gives NaN).                                               */
+void or_softmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy);
+
 /* Worker threads used by the parallel loops (0 = all online CPUs). */
 void or_set_threads(int32_t n);
 int32_t or_get_threads(void);
