@@ -36,6 +36,7 @@
 #ifndef MP_H
 #define MP_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -295,6 +296,61 @@ mp_status mp_absmax(const mp_tensor_list* list, float* amax, uint32_t* nonfinite
  * dynamic. Errors: MP_ERR_INVALID_ARGUMENT. */
 mp_status mp_scaler_init_from_absmax(mp_scaler* scaler, const float* amax, float headroom,
                                      int32_t dynamic, int32_t growth_interval, mp_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Large reductions. Source: the analysis page, §3.4 "FP16 Arithmetic with
+ * FP32 Accumulation": batch normalization's mean and variance and the
+ * softmax normalization constant are summed in FP32 from binary16 tensors,
+ * all of their arithmetic is FP32, and binary16 results are written back.
+ * Matrices are row-major with a row pitch (ld*) in elements, ld >= columns.
+ * The sums run in a fixed order, so results do not vary from run to run;
+ * that order is not the sequential one, so they are not bit-equal to a
+ * sequential FP32 sum. Every entry point is asynchronous on `stream`.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace mp_bn_stats needs for these sizes (0 when there
+ * is nothing to do). */
+size_t mp_bn_stats_workspace(int64_t rows, int64_t channels);
+
+/* Batch-normalization statistics of x[rows, channels] (binary16; channels
+ * contiguous, e.g. NHWC with rows = N*H*W): per channel, mean = sum(x) / rows
+ * and the population variance var = sum((x - mean)^2) / rows, written as FP32
+ * to the device arrays mean[channels] and var[channels]. Computed in FP32 with
+ * Welford's update per thread and Chan's pairwise merge, in a fixed order.
+ * `workspace` is caller-owned device memory of at least
+ * mp_bn_stats_workspace(rows, channels) bytes, 4-byte aligned, overwritten.
+ * Errors: MP_ERR_INVALID_ARGUMENT (rows < 1, channels < 0, ldx < channels, a
+ * null pointer or too small a workspace when channels > 0), MP_ERR_HIP. */
+mp_status mp_bn_stats(const uint16_t* x, int64_t rows, int64_t channels, int64_t ldx, float* mean,
+                      float* var, void* workspace, size_t workspace_bytes, mp_stream stream);
+
+/* Batch-normalization: y = RNE16(((x - mean) * inv) * gamma + beta) with
+ * inv = 1 / sqrt(var + eps) per channel: FP32, one rounding per operation in
+ * this order (correctly rounded square root and division), then round to
+ * nearest even binary16. mean, var, gamma, beta: device FP32 [channels].
+ * x and y may not overlap unless x == y with ldx == ldy.
+ * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, ldx or ldy < channels, a
+ * null pointer with rows * channels > 0), MP_ERR_HIP. */
+mp_status mp_bn_apply(const uint16_t* x, int64_t rows, int64_t channels, int64_t ldx, const float* mean,
+                      const float* var, const float* gamma, const float* beta, float eps, uint16_t* y,
+                      int64_t ldy, mp_stream stream);
+
+/* Bytes of device workspace mp_softmax needs for these sizes (0 when there is
+ * nothing to do). */
+size_t mp_softmax_workspace(int64_t rows, int64_t cols);
+
+/* Row-wise softmax of x[rows, cols] (binary16): y = RNE16(exp(x - m) / s), m
+ * the row maximum and s the sum of exp(x - m) over the row, in FP32 (the
+ * quotient as exp(x - m) * (1 / s)). Rows are cut into segments merged in a
+ * fixed order. A row containing NaN or +inf gives NaN throughout; -inf entries
+ * give 0, and a row of only -inf gives NaN. `workspace`: caller-owned device
+ * memory of at least mp_softmax_workspace(rows, cols) bytes, 8-byte aligned,
+ * overwritten. x and y may be the same matrix (ldx == ldy); no other overlap.
+ * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, rows > 2^31 - 1, ldx or ldy
+ * < cols, a null pointer or too small a workspace when rows * cols > 0),
+ * MP_ERR_HIP. */
+mp_status mp_softmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, mp_stream stream);
 
 /* ------------------------------------------------------------------------
  * Auxiliary steps that a full training step needs around the hot path.

@@ -89,6 +89,13 @@ def lib() -> C.CDLL:
         L.mp_act_bwd.argtypes = [C.c_int, vp, vp, vp, i64, vp]
         L.mp_loss_softmax_ce.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
         L.mp_loss_mse.argtypes = [vp, vp, i64, i64, C.c_float, vp, vp, vp, vp]
+        L.mp_bn_stats_workspace.argtypes = [i64, i64]
+        L.mp_bn_stats_workspace.restype = C.c_size_t
+        L.mp_bn_stats.argtypes = [vp, i64, i64, i64, vp, vp, vp, C.c_size_t, vp]
+        L.mp_bn_apply.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, C.c_float, vp, i64, vp]
+        L.mp_softmax_workspace.argtypes = [i64, i64]
+        L.mp_softmax_workspace.restype = C.c_size_t
+        L.mp_softmax.argtypes = [vp, i64, i64, i64, vp, i64, vp, C.c_size_t, vp]
         L.mp_status_string.argtypes = [C.c_int]
         L.mp_status_string.restype = C.c_char_p
         L.mp_last_hip_error.restype = C.c_char_p
@@ -96,7 +103,7 @@ def lib() -> C.CDLL:
         for name in ("mp_linear_fwd", "mp_linear_dgrad", "mp_linear_wgrad", "mp_param_list_create",
                      "mp_param_list_destroy", "mp_step", "mp_scaler_init", "mp_scaler_update",
                      "mp_round_f32_to_f16", "mp_act_fwd", "mp_act_bwd", "mp_loss_softmax_ce",
-                     "mp_loss_mse"):
+                     "mp_loss_mse", "mp_bn_stats", "mp_bn_apply", "mp_softmax"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -105,7 +112,7 @@ def lib() -> C.CDLL:
 def header_functions() -> list[str]:
     """Names of every function declared in include/mp.h."""
     text = open(HEADER_PATH).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|mp_status|int64_t)\s+(mp_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|mp_status|int64_t|size_t)\s+(mp_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -402,6 +409,61 @@ def act_bwd(kind: int, x: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor | Non
     _check(lib().mp_act_bwd(int(kind), C.c_void_p(x.data_ptr()), C.c_void_p(dy.data_ptr()),
                             C.c_void_p(dx.data_ptr()), x.numel(), _stream(stream)), "mp_act_bwd")
     return dx
+
+
+# ------------------------------------------------------------------ large reductions
+def _f32vec(t: torch.Tensor, name: str, n: int) -> C.c_void_p:
+    _dev(t, name, 4)
+    if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    return C.c_void_p(t.data_ptr())
+
+
+def bn_stats(x: torch.Tensor, mean: torch.Tensor | None = None, var: torch.Tensor | None = None,
+             stream=None):
+    """Per-channel mean and population variance (FP32) of x[rows, channels] (binary16)."""
+    rows, ch = x.shape
+    px, ldx = _mat(x, "x")
+    mean = _out(mean, (ch,), torch.float32, x.device)
+    var = _out(var, (ch,), torch.float32, x.device)
+    nbytes = int(lib().mp_bn_stats_workspace(rows, ch))
+    ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=x.device)
+    _check(lib().mp_bn_stats(px, rows, ch, ldx, _f32vec(mean, "mean", ch), _f32vec(var, "var", ch),
+                             C.c_void_p(ws.data_ptr()), nbytes, _stream(stream)), "mp_bn_stats")
+    return mean, var
+
+
+def bn_apply(x: torch.Tensor, mean: torch.Tensor, var: torch.Tensor, gamma: torch.Tensor,
+             beta: torch.Tensor, eps: float, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = RNE16(((x - mean) * (1 / sqrt(var + eps))) * gamma + beta), per channel, FP32."""
+    rows, ch = x.shape
+    y = _rows_out(y, rows, ch, x)
+    px, ldx = _mat(x, "x"); py, ldy = _mat(y, "y")
+    _check(lib().mp_bn_apply(px, rows, ch, ldx, _f32vec(mean, "mean", ch), _f32vec(var, "var", ch),
+                             _f32vec(gamma, "gamma", ch), _f32vec(beta, "beta", ch), float(eps), py, ldy,
+                             _stream(stream)), "mp_bn_apply")
+    return y
+
+
+def _rows_out(y, rows: int, cols: int, like: torch.Tensor) -> torch.Tensor:
+    """y, or a new [rows, cols] matrix whose row pitch is cols rounded up to 8 elements, so
+    its rows are 16-byte aligned (the kernels' 16-byte path)."""
+    if y is not None:
+        return y
+    ld = (cols + 7) // 8 * 8
+    return torch.empty((rows, ld), dtype=like.dtype, device=like.device)[:, :cols]
+
+
+def softmax(x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-wise softmax of x[rows, cols] (binary16 in and out, FP32 arithmetic)."""
+    rows, cols = x.shape
+    y = _rows_out(y, rows, cols, x)
+    px, ldx = _mat(x, "x"); py, ldy = _mat(y, "y")
+    nbytes = int(lib().mp_softmax_workspace(rows, cols))
+    ws = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
+    _check(lib().mp_softmax(px, rows, cols, ldx, py, ldy, C.c_void_p(ws.data_ptr()), nbytes,
+                            _stream(stream)), "mp_softmax")
+    return y
 
 
 def loss_softmax_ce(logits: torch.Tensor, labels: torch.Tensor, scaler: Scaler,

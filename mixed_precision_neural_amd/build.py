@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmp.so")
-SOURCES = ["mp_common.hip", "mp_step.hip", "mp_gemm.hip", "mp_aux.hip", "mp_stats.hip"]
+SOURCES = ["mp_common.hip", "mp_step.hip", "mp_gemm.hip", "mp_aux.hip", "mp_stats.hip", "mp_reduce.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

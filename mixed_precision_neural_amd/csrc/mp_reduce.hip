@@ -1,0 +1,458 @@
+// Large reductions on gfx950: batch-normalization statistics and normalization,
+// and the row softmax, reading and writing binary16 with FP32 arithmetic.
+//
+// Source: "Mixed Precision Training", long-form analysis page
+// (paper-graph-ui.vercel.app), §3.4 "FP16 Arithmetic with FP32 Accumulation":
+// large reductions (batch normalization's mean and variance over the batch and
+// spatial positions, the softmax normalization constant) are summed in FP32
+// from binary16 tensors, all of their arithmetic is FP32 and binary16 results
+// are written back; these layers are memory-bound, so FP32 costs no time.
+//
+// Design (HBM-bound; 16-byte loads and stores where rows are 16-byte aligned,
+// an element-wise path with the same arithmetic otherwise):
+//   - Batch-norm statistics of x[rows, C]: a block owns a chunk of rows and up
+//     to 256 groups of 8 channels; each thread keeps Welford's running mean and
+//     sum of squared deviations (M2) in FP32 for its 8 channels over its rows
+//     of the chunk, the block merges its row lanes with Chan's pairwise formula
+//     in a fixed tree, and writes one (count, mean, M2) per channel and chunk
+//     to the caller's workspace. A second kernel merges the chunks of each
+//     channel in a fixed order (one block per channel) and writes mean and the
+//     population variance M2 / rows. Results do not depend on timing.
+//   - The normalization y = ((x - mean) * inv) * gamma + beta, inv = 1 /
+//     sqrt(var + eps) per channel (correctly rounded square root and
+//     division), one rounding per operation in that order, then
+//     round-to-nearest-even binary16.
+//   - Softmax of each row of x[rows, cols]: the row is cut into segments; one
+//     block per (row, segment) keeps an online (max m, sum s of exp(x - m)) per
+//     thread, merges the block's pairs in a fixed tree and writes them to the
+//     workspace. The second kernel has every block of a row merge the row's
+//     pairs in the same fixed order (so all agree on (M, S) to the bit) and
+//     write RNE16(exp(x - M) * (1 / S)) for its segment. m starts at -FLT_MAX,
+//     so -inf entries give exp = 0 without NaN; a NaN or +inf entry makes the
+//     row's sum NaN, and a row of only -inf gives 0 / 0 = NaN.
+#include <float.h>
+
+#include "mp_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------ statistics
+struct Moments {
+    float n, mean, m2;
+};
+
+// Chan et al.'s pairwise update: the moments of the union of two disjoint sets.
+__device__ __forceinline__ Moments merge(Moments a, Moments b) {
+    if (b.n == 0.0f) return a;
+    if (a.n == 0.0f) return b;
+    const float n = a.n + b.n;
+    const float fb = b.n / n;
+    const float d = b.mean - a.mean;
+    Moments r;
+    r.n = n;
+    r.mean = a.mean + d * fb;
+    r.m2 = (a.m2 + b.m2) + (d * d) * (a.n * fb);
+    return r;
+}
+
+// Loads VEC consecutive binary16 values as floats.
+template <int VEC>
+__device__ __forceinline__ void load_f16(const uint16_t* p, float (&v)[VEC]) {
+    if constexpr (VEC == 8) {
+        const mp::u32x4 w = *mp::global(reinterpret_cast<const mp::u32x4*>(p));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = mp::h2f(uint16_t(w[k >> 1] >> ((k & 1) * 16)));
+    } else {
+        v[0] = mp::h2f(*mp::global(p));
+    }
+}
+
+// Thread layout of the two batch-norm kernels: lanes (row lane rl, channel
+// group g) over the block's channel groups; rows_per_iter row lanes.
+struct BnLayout {
+    int g, rl, lc, rp;
+    bool active;
+    __device__ __forceinline__ BnLayout(int groups_left) {
+        lc = groups_left < kThreads ? groups_left : kThreads;
+        rp = kThreads / lc;
+        const int t = int(threadIdx.x);
+        g = t % lc;
+        rl = t / lc;
+        active = rl < rp;
+    }
+};
+
+// grid (chunks, channel blocks); ws: cnt[chunks], mean[chunks][C], m2[chunks][C]
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void bn_partial_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                              int64_t C, int64_t ldx, int64_t rows_per_chunk,
+                                                              float* __restrict__ ws) {
+    const int64_t groups = C / VEC;
+    const int64_t g0 = int64_t(blockIdx.y) * kThreads;
+    const BnLayout L(int(groups - g0 < kThreads ? groups - g0 : kThreads));
+    const int64_t r0 = int64_t(blockIdx.x) * rows_per_chunk;
+    const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
+    const int64_t c0 = (g0 + L.g) * VEC;
+
+    float n = 0.0f, mean[VEC], m2[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) mean[k] = m2[k] = 0.0f;
+    if (L.active) {
+        // Welford over this lane's rows, four rows' loads issued before their updates
+        int64_t r = r0 + L.rl;
+        for (; r + 3 * L.rp < r1; r += 4 * L.rp) {
+            float v[4][VEC];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load_f16<VEC>(x + (r + u * L.rp) * ldx + c0, v[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                n += 1.0f;
+                const float inv = 1.0f / n;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float d = v[u][k] - mean[k];
+                    mean[k] = mean[k] + d * inv;
+                    m2[k] = m2[k] + d * (v[u][k] - mean[k]);
+                }
+            }
+        }
+        for (; r < r1; r += L.rp) {
+            float v[VEC];
+            load_f16<VEC>(x + r * ldx + c0, v);
+            n += 1.0f;
+            const float inv = 1.0f / n;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float d = v[k] - mean[k];
+                mean[k] = mean[k] + d * inv;
+                m2[k] = m2[k] + d * (v[k] - mean[k]);
+            }
+        }
+    }
+
+    // merge the row lanes of each channel group: a fixed binary tree over rl
+    __shared__ float s_n[kThreads], s_mean[VEC][kThreads], s_m2[VEC][kThreads];
+    const int t = int(threadIdx.x);
+    s_n[t] = n;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) { s_mean[k][t] = mean[k]; s_m2[k][t] = m2[k]; }
+    __syncthreads();
+    for (int s = 1; s < L.rp; s *= 2) {
+        if (L.active && (L.rl % (2 * s)) == 0 && L.rl + s < L.rp) {
+            const int o = t + s * L.lc;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const Moments m = merge({s_n[t], s_mean[k][t], s_m2[k][t]}, {s_n[o], s_mean[k][o], s_m2[k][o]});
+                s_mean[k][t] = m.mean;
+                s_m2[k][t] = m.m2;
+            }
+            s_n[t] = s_n[t] + s_n[o];
+        }
+        __syncthreads();
+    }
+    if (L.active && L.rl == 0) {
+        float* wmean = ws + gridDim.x + int64_t(blockIdx.x) * C;
+        float* wm2 = ws + gridDim.x + int64_t(gridDim.x) * C + int64_t(blockIdx.x) * C;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            wmean[c0 + k] = s_mean[k][t];
+            wm2[c0 + k] = s_m2[k][t];
+        }
+        if (blockIdx.y == 0 && L.g == 0) ws[blockIdx.x] = s_n[t];
+    }
+}
+
+// One block per channel: merges the chunks' moments in a fixed order.
+__global__ __launch_bounds__(kThreads) void bn_final_kernel(const float* __restrict__ ws, int64_t chunks, int64_t C,
+                                                            float* __restrict__ mean, float* __restrict__ var) {
+    const int64_t c = blockIdx.x;
+    const int t = int(threadIdx.x);
+    const float* wmean = ws + chunks;
+    const float* wm2 = ws + chunks + chunks * C;
+    Moments acc = {0.0f, 0.0f, 0.0f};
+    for (int64_t k = t; k < chunks; k += kThreads) acc = merge(acc, {ws[k], wmean[k * C + c], wm2[k * C + c]});
+    __shared__ float s_n[kThreads], s_mean[kThreads], s_m2[kThreads];
+    s_n[t] = acc.n; s_mean[t] = acc.mean; s_m2[t] = acc.m2;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s /= 2) {
+        if (t < s) {
+            const Moments m = merge({s_n[t], s_mean[t], s_m2[t]}, {s_n[t + s], s_mean[t + s], s_m2[t + s]});
+            s_n[t] = m.n; s_mean[t] = m.mean; s_m2[t] = m.m2;
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        mean[c] = s_mean[0];
+        var[c] = s_m2[0] / s_n[0];
+    }
+}
+
+// ------------------------------------------------------------------ normalization
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void bn_apply_kernel(const uint16_t* x, int64_t rows, int64_t C,
+                                                            int64_t ldx, const float* __restrict__ mean,
+                                                            const float* __restrict__ var,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta, float eps,
+                                                            uint16_t* y, int64_t ldy,
+                                                            int64_t rows_per_chunk) {
+    const int64_t groups = C / VEC;
+    const int64_t g0 = int64_t(blockIdx.y) * kThreads;
+    const BnLayout L(int(groups - g0 < kThreads ? groups - g0 : kThreads));
+    if (!L.active) return;
+    const int64_t c0 = (g0 + L.g) * VEC;
+    float mu[VEC], inv[VEC], ga[VEC], be[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        const float s = var[c0 + k] + eps;
+        const float r = sqrtf(s);
+        inv[k] = 1.0f / r;
+        mu[k] = mean[c0 + k];
+        ga[k] = gamma[c0 + k];
+        be[k] = beta[c0 + k];
+    }
+    const int64_t r0 = int64_t(blockIdx.x) * rows_per_chunk;
+    const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
+    for (int64_t r = r0 + L.rl; r < r1; r += L.rp) {
+        float v[VEC];
+        load_f16<VEC>(x + r * ldx + c0, v);
+        uint16_t h[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float t = v[k] - mu[k];
+            const float u = t * inv[k];
+            const float w = u * ga[k];
+            h[k] = mp::f2h(w + be[k]);
+        }
+        if constexpr (VEC == 8) {
+            *mp::global(reinterpret_cast<mp::u32x4*>(y + r * ldy + c0)) =
+                mp::u32x4{uint32_t(h[0]) | uint32_t(h[1]) << 16, uint32_t(h[2]) | uint32_t(h[3]) << 16,
+                          uint32_t(h[4]) | uint32_t(h[5]) << 16, uint32_t(h[6]) | uint32_t(h[7]) << 16};
+        } else {
+            *mp::global(y + r * ldy + c0) = h[0];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ softmax
+struct MaxSum {
+    float m, s;
+};
+
+__device__ __forceinline__ MaxSum merge(MaxSum a, MaxSum b) {
+    const float m = fmaxf(a.m, b.m);
+    return {m, a.s * __expf(a.m - m) + b.s * __expf(b.m - m)};
+}
+
+// Merges the 256 threads' pairs in a fixed tree; every thread gets the result.
+__device__ __forceinline__ MaxSum block_merge(MaxSum v) {
+    __shared__ float s_m[kThreads], s_s[kThreads];
+    const int t = int(threadIdx.x);
+    s_m[t] = v.m; s_s[t] = v.s;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s /= 2) {
+        if (t < s) {
+            const MaxSum r = merge(MaxSum{s_m[t], s_s[t]}, MaxSum{s_m[t + s], s_s[t + s]});
+            s_m[t] = r.m; s_s[t] = r.s;
+        }
+        __syncthreads();
+    }
+    const MaxSum r = {s_m[0], s_s[0]};
+    __syncthreads();
+    return r;
+}
+
+// Segment seg of a row covers vectors [seg * seg_vecs, ...) of the row's full
+// VEC-element vectors; the last segment also takes the row's tail elements.
+struct Segment {
+    int64_t v0, v1, tail0, tail1;
+    __device__ __forceinline__ Segment(int64_t cols, int vec, int64_t seg_vecs) {
+        const int64_t nvec = cols / vec;
+        const int64_t seg = blockIdx.y;
+        v0 = seg * seg_vecs;
+        v1 = v0 + seg_vecs < nvec ? v0 + seg_vecs : nvec;
+        const bool last = seg == int64_t(gridDim.y) - 1;
+        tail0 = last ? nvec * vec : cols;
+        tail1 = cols;
+    }
+};
+
+// grid (rows, segments): one (max, sum) per (row, segment) in ws[row * segments + seg]
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void softmax_partial_kernel(const uint16_t* __restrict__ x, int64_t cols,
+                                                                   int64_t ldx, int64_t seg_vecs,
+                                                                   float2* __restrict__ ws) {
+    const int64_t row = blockIdx.x;
+    const uint16_t* xr = x + row * ldx;
+    const Segment sg(cols, VEC, seg_vecs);
+    MaxSum acc = {-FLT_MAX, 0.0f};
+    for (int64_t v = sg.v0 + threadIdx.x; v < sg.v1; v += kThreads) {
+        float e[VEC];
+        load_f16<VEC>(xr + v * VEC, e);
+        float vm = e[0];
+#pragma unroll
+        for (int k = 1; k < VEC; ++k) vm = fmaxf(vm, e[k]);
+        if (vm > acc.m) {
+            acc.s = acc.s * __expf(acc.m - vm);
+            acc.m = vm;
+        }
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc.s = acc.s + __expf(e[k] - acc.m);
+    }
+    for (int64_t j = sg.tail0 + threadIdx.x; j < sg.tail1; j += kThreads) {
+        const float e = mp::h2f(*mp::global(xr + j));
+        if (e > acc.m) {
+            acc.s = acc.s * __expf(acc.m - e);
+            acc.m = e;
+        }
+        acc.s = acc.s + __expf(e - acc.m);
+    }
+    const MaxSum r = block_merge(acc);
+    if (threadIdx.x == 0) ws[row * gridDim.y + blockIdx.y] = make_float2(r.m, r.s);
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void softmax_norm_kernel(const uint16_t* x, int64_t cols,
+                                                                int64_t ldx, uint16_t* y, int64_t ldy,
+                                                                int64_t seg_vecs, const float2* __restrict__ ws) {
+    const int64_t row = blockIdx.x;
+    const int64_t S = gridDim.y;
+    // the row's pairs, merged in the same order by every block of the row
+    MaxSum acc = {-FLT_MAX, 0.0f};
+    for (int64_t k = threadIdx.x; k < S; k += kThreads) {
+        const float2 p = ws[row * S + k];
+        acc = merge(acc, MaxSum{p.x, p.y});
+    }
+    const MaxSum tot = block_merge(acc);
+    const float inv = 1.0f / tot.s;
+    const uint16_t* xr = x + row * ldx;
+    uint16_t* yr = y + row * ldy;
+    const Segment sg(cols, VEC, seg_vecs);
+    for (int64_t v = sg.v0 + threadIdx.x; v < sg.v1; v += kThreads) {
+        float e[VEC];
+        load_f16<VEC>(xr + v * VEC, e);
+        uint16_t h[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) h[k] = mp::f2h(__expf(e[k] - tot.m) * inv);
+        if constexpr (VEC == 8) {
+            *mp::global(reinterpret_cast<mp::u32x4*>(yr + v * VEC)) =
+                mp::u32x4{uint32_t(h[0]) | uint32_t(h[1]) << 16, uint32_t(h[2]) | uint32_t(h[3]) << 16,
+                          uint32_t(h[4]) | uint32_t(h[5]) << 16, uint32_t(h[6]) | uint32_t(h[7]) << 16};
+        } else {
+            *mp::global(yr + v) = h[0];
+        }
+    }
+    for (int64_t j = sg.tail0 + threadIdx.x; j < sg.tail1; j += kThreads)
+        *mp::global(yr + j) = mp::f2h(__expf(mp::h2f(*mp::global(xr + j)) - tot.m) * inv);
+}
+
+// ------------------------------------------------------------------ shapes
+constexpr int64_t kMaxChunks = 1024;
+
+// Rows per chunk of the batch-norm kernels: at least four row iterations per
+// thread, at most kMaxChunks chunks.
+int64_t bn_rows_per_chunk(int64_t rows, int64_t C, int vec) {
+    const int64_t groups = C / vec > 0 ? C / vec : 1;
+    const int64_t lc = groups < kThreads ? groups : kThreads;
+    const int64_t rp = kThreads / lc;
+    int64_t per = (rows + kMaxChunks - 1) / kMaxChunks;
+    if (per < 4 * rp) per = 4 * rp;
+    return (per + rp - 1) / rp * rp;
+}
+
+int bn_vec(const void* x, int64_t ldx, int64_t C, const void* y = nullptr, int64_t ldy = 0) {
+    const bool ok = (C % 8) == 0 && (ldx % 8) == 0 && mp::aligned16(x) && (y == nullptr || (mp::aligned16(y) && (ldy % 8) == 0));
+    return ok ? 8 : 1;
+}
+
+int64_t softmax_segments(int64_t cols) {
+    int64_t s = (cols + 8191) / 8192;
+    return s < 1 ? 1 : (s > 1024 ? 1024 : s);
+}
+
+}  // namespace
+
+// Enough for either path (the 16-byte path is chosen at launch from the pointers).
+extern "C" size_t mp_bn_stats_workspace(int64_t rows, int64_t channels) {
+    if (rows <= 0 || channels <= 0) return 0;
+    int64_t c = 0;
+    for (int vec : {1, 8}) {
+        const int64_t per = bn_rows_per_chunk(rows, channels, vec);
+        const int64_t k = (rows + per - 1) / per;
+        c = k > c ? k : c;
+    }
+    return size_t(c * (2 * channels + 1)) * sizeof(float);
+}
+
+extern "C" mp_status mp_bn_stats(const uint16_t* x, int64_t rows, int64_t channels, int64_t ldx, float* mean,
+                                 float* var, void* workspace, size_t workspace_bytes, mp_stream stream) {
+    if (rows <= 0 || channels < 0 || ldx < channels) return MP_ERR_INVALID_ARGUMENT;
+    if (channels == 0) return MP_OK;
+    if (!x || !mean || !var || !workspace || workspace_bytes < mp_bn_stats_workspace(rows, channels))
+        return MP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = mp::as_stream(stream);
+    const int vec = bn_vec(x, ldx, channels);
+    const int64_t per = bn_rows_per_chunk(rows, channels, vec);
+    const int64_t chunks = (rows + per - 1) / per;
+    const int64_t cblocks = (channels / vec + kThreads - 1) / kThreads;
+    float* ws = static_cast<float*>(workspace);
+    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(cblocks));
+    if (vec == 8)
+        bn_partial_kernel<8><<<grid, kThreads, 0, s>>>(x, rows, channels, ldx, per, ws);
+    else
+        bn_partial_kernel<1><<<grid, kThreads, 0, s>>>(x, rows, channels, ldx, per, ws);
+    mp_status st = mp::launch_status("bn_partial_kernel");
+    if (st != MP_OK) return st;
+    bn_final_kernel<<<unsigned(channels), kThreads, 0, s>>>(ws, chunks, channels, mean, var);
+    return mp::launch_status("bn_final_kernel");
+}
+
+extern "C" mp_status mp_bn_apply(const uint16_t* x, int64_t rows, int64_t channels, int64_t ldx, const float* mean,
+                                 const float* var, const float* gamma, const float* beta, float eps, uint16_t* y,
+                                 int64_t ldy, mp_stream stream) {
+    if (rows < 0 || channels < 0 || ldx < channels || ldy < channels) return MP_ERR_INVALID_ARGUMENT;
+    if (rows == 0 || channels == 0) return MP_OK;
+    if (!x || !mean || !var || !gamma || !beta || !y) return MP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = mp::as_stream(stream);
+    const int vec = bn_vec(x, ldx, channels, y, ldy);
+    const int64_t per = bn_rows_per_chunk(rows, channels, vec);
+    const dim3 grid(unsigned((rows + per - 1) / per), unsigned((channels / vec + kThreads - 1) / kThreads));
+    if (vec == 8)
+        bn_apply_kernel<8><<<grid, kThreads, 0, s>>>(x, rows, channels, ldx, mean, var, gamma, beta, eps, y, ldy, per);
+    else
+        bn_apply_kernel<1><<<grid, kThreads, 0, s>>>(x, rows, channels, ldx, mean, var, gamma, beta, eps, y, ldy, per);
+    return mp::launch_status("bn_apply_kernel");
+}
+
+extern "C" size_t mp_softmax_workspace(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return size_t(rows * softmax_segments(cols)) * sizeof(float2);
+}
+
+extern "C" mp_status mp_softmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                                void* workspace, size_t workspace_bytes, mp_stream stream) {
+    if (rows < 0 || cols < 0 || ldx < cols || ldy < cols) return MP_ERR_INVALID_ARGUMENT;
+    if (rows == 0 || cols == 0) return MP_OK;
+    if (!x || !y || !workspace || workspace_bytes < mp_softmax_workspace(rows, cols)) return MP_ERR_INVALID_ARGUMENT;
+    if (rows > 0x7FFFFFFF) return MP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = mp::as_stream(stream);
+    const int vec = (mp::aligned16(x) && mp::aligned16(y) && ldx % 8 == 0 && ldy % 8 == 0) ? 8 : 1;
+    const int64_t S = softmax_segments(cols);
+    const int64_t nvec = cols / vec;
+    const int64_t seg_vecs = (nvec + S - 1) / S;
+    const dim3 grid(static_cast<unsigned>(rows), static_cast<unsigned>(S));
+    float2* ws = static_cast<float2*>(workspace);
+    if (vec == 8)
+        softmax_partial_kernel<8><<<grid, kThreads, 0, s>>>(x, cols, ldx, seg_vecs, ws);
+    else
+        softmax_partial_kernel<1><<<grid, kThreads, 0, s>>>(x, cols, ldx, seg_vecs, ws);
+    mp_status st = mp::launch_status("softmax_partial_kernel");
+    if (st != MP_OK) return st;
+    if (vec == 8)
+        softmax_norm_kernel<8><<<grid, kThreads, 0, s>>>(x, cols, ldx, y, ldy, seg_vecs, ws);
+    else
+        softmax_norm_kernel<1><<<grid, kThreads, 0, s>>>(x, cols, ldx, y, ldy, seg_vecs, ws);
+    return mp::launch_status("softmax_norm_kernel");
+}

@@ -54,7 +54,7 @@ def kernel_bodies(asm):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("name", ["mp_step", "mp_aux", "mp_gemm"])
+@pytest.mark.parametrize("name", ["mp_step", "mp_aux", "mp_gemm", "mp_reduce"])
 def test_no_mixed_precision_fma(name, tmp_path):
     asm = device_asm(name, tmp_path)
     assert "v_fma_mix" not in asm and "v_mad_mix" not in asm
@@ -76,3 +76,16 @@ def test_update_kernel_has_no_fused_multiply_add(tmp_path):
         else:
             assert "v_div_fixup_f32" in body and "v_div_fmas_f32" in body, sym
             assert "v_fma_mix" not in body, sym
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_bn_apply_uses_correctly_rounded_sqrt_and_division(tmp_path):
+    """The batch-norm normalization computes 1 / sqrt(var + eps) with a correctly rounded square
+    root (v_sqrt_f32 refined by its residual, with the scaling for small inputs) and the IEEE
+    division sequence, so its bits match the oracle's FP32 sqrtf and division."""
+    bodies = kernel_bodies(device_asm("mp_reduce", tmp_path))
+    apply = {k: v for k, v in bodies.items() if "bn_apply_kernel" in k}
+    assert len(apply) == 2, sorted(apply)
+    for sym, body in apply.items():
+        assert "v_sqrt_f32" in body and re.search(r"v_fma_f32 v\d+, -v\d+, v\d+, v\d+", body), sym
+        assert "v_div_fixup_f32" in body and "v_div_fmas_f32" in body, sym
