@@ -49,11 +49,17 @@ MEASURED_TRAFFIC = {
                "sha256": "d86b62e4996178e358f210919c4924b451ef3cfd11eb4e7fd813d5603ebb303b",
                "update": (991536.1, 1972664.4), "nesterov": (990696.8, 1973870.8),
                "adagrad": (993424.8, 1969782.5)},
+    "reduce": {"src": ["mp_reduce.hip", "mp_internal.h"], "sha256": ""},
     "stats": {"src": ["mp_stats.hip", "mp_internal.h"],
               "sha256": "79a9d4df03ca2e0bc26ef9ad12997727b98bc8794de1120c401d16191dc07d82",
               "absmax": (394787.2, 7.6)},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+# The large reductions at the pages' sizes: batch normalization over 32 images x 112 x 112
+# positions x 64 channels, and the softmax over the 793,471-word vocabulary (64 rows, row pitch
+# rounded up to 8 elements).
+BN_ROWS, BN_CH = 32 * 112 * 112, 64
+SM_ROWS, SM_COLS = 64, 793471
 
 
 def parse():
@@ -66,7 +72,7 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="GELU as separate point-wise kernels instead of in the GEMM epilogues")
     p.add_argument("--pmc-kernel", choices=["fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad", "update", "update_nesterov",
-                            "update_adagrad", "absmax", "copy"],
+                            "update_adagrad", "absmax", "bn_stats", "bn_apply", "softmax", "copy"],
                    help="only launch this kernel --pmc-reps times at the bench's shape (for counter passes)")
     p.add_argument("--pmc-reps", type=int, default=3)
     return p.parse_args()
@@ -115,6 +121,8 @@ def pmc_kernel(args, mp, torch):
         x = torch.randn(LAYERS * n * n, device="cuda")
         tl = mp.TensorList([x]); amax = torch.zeros(1, device="cuda")
         f = lambda: mp.absmax(tl, amax)
+    elif args.pmc_kernel in ("bn_stats", "bn_apply", "softmax"):
+        f = reduction_calls(mp, torch)[args.pmc_kernel]
     else:                                   # calibration: 1 GiB read + 1 GiB written per launch
         x = torch.randn(256 * 1024 * 1024, device="cuda"); y = torch.empty_like(x)
         f = lambda: y.copy_(x)
@@ -122,6 +130,47 @@ def pmc_kernel(args, mp, torch):
         f()
     torch.cuda.synchronize()
     print(json.dumps({"pmc_kernel": args.pmc_kernel, "launches": args.pmc_reps}), flush=True)
+
+
+def reduction_calls(mp, torch) -> dict:
+    """One call of each large reduction on synthetic inputs of the pages' sizes (outputs
+    preallocated; the first call of each is made here, untimed)."""
+    g = torch.Generator(device="cuda").manual_seed(1)
+    x = (torch.randn(BN_ROWS, BN_CH, device="cuda", generator=g) * 2.0 + 0.5).half()
+    mean = torch.empty(BN_CH, device="cuda"); var = torch.empty(BN_CH, device="cuda")
+    gamma = torch.ones(BN_CH, device="cuda"); beta = torch.zeros(BN_CH, device="cuda")
+    y = torch.empty_like(x)
+    ld = (SM_COLS + 7) // 8 * 8
+    xs = (torch.randn(SM_ROWS, ld, device="cuda", generator=g) * 3.0).half()[:, :SM_COLS]
+    ys = torch.empty(SM_ROWS, ld, device="cuda", dtype=torch.float16)[:, :SM_COLS]
+    calls = {"bn_stats": lambda: mp.bn_stats(x, mean, var),
+             "bn_apply": lambda: mp.bn_apply(x, mean, var, gamma, beta, 1e-5, y=y),
+             "softmax": lambda: mp.softmax(xs, y=ys)}
+    for f in calls.values():
+        f()
+    return calls
+
+
+def reductions(model, mp, torch) -> dict:
+    """The large reductions: HIP-event time per call over 10 calls, GB/s on the algorithmic
+    bytes (statistics: 2 B per value read; normalization and softmax: 2 read + 2 written; the
+    softmax's second read of x is implementation traffic)."""
+    calls = reduction_calls(mp, torch)
+    out = {}
+    for name, f in calls.items():
+        model.events = {}
+        for _ in range(10):
+            model._t(name, f)
+        torch.cuda.synchronize()
+        ms = model.kernel_ms()[name]["avg_ms"]
+        n = BN_ROWS * BN_CH if name != "softmax" else SM_ROWS * SM_COLS
+        nbytes = (2 if name == "bn_stats" else 4) * n
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"shape": [BN_ROWS, BN_CH] if name != "softmax" else [SM_ROWS, SM_COLS],
+                     "avg_us": round(ms * 1e3, 2), "achieved_GBps": round(gbps, 1),
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nbytes,
+                     "traffic": measured_traffic("reduce", name)}
+    return out
 
 
 def calibration_c() -> float:
@@ -348,6 +397,7 @@ def main():
                "traffic": measured_traffic("stats", "absmax"), "input": "FP32, 12 x 4096^2"}
     tl.close()
     del g_w, g_s, g_16
+    fp32_reductions = reductions(model, mp, torch)
 
     gemm_flop = 2.0 * WIDTH * WIDTH * BATCH
     step_flop = gemm_flop * (3 * LAYERS - 1)
@@ -396,6 +446,7 @@ def main():
                     "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam},
         "mp_step_opt": variants,
         "absmax_method2": method2,
+        "fp32_reductions": fp32_reductions,
         "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")
                    if k in kern},
         "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},

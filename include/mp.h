@@ -316,7 +316,8 @@ size_t mp_bn_stats_workspace(int64_t rows, int64_t channels);
  * contiguous, e.g. NHWC with rows = N*H*W): per channel, mean = sum(x) / rows
  * and the population variance var = sum((x - mean)^2) / rows, written as FP32
  * to the device arrays mean[channels] and var[channels]. Computed in FP32 with
- * Welford's update per thread and Chan's pairwise merge, in a fixed order.
+ * per-thread sums of shifted values (the shift is one of the thread's own
+ * values) and Chan's pairwise merge, in a fixed order.
  * `workspace` is caller-owned device memory of at least
  * mp_bn_stats_workspace(rows, channels) bytes, 4-byte aligned, overwritten.
  * Errors: MP_ERR_INVALID_ARGUMENT (rows < 1, channels < 0, ldx < channels, a

@@ -11,9 +11,10 @@
 // Design (HBM-bound; 16-byte loads and stores where rows are 16-byte aligned,
 // an element-wise path with the same arithmetic otherwise):
 //   - Batch-norm statistics of x[rows, C]: a block owns a chunk of rows and up
-//     to 256 groups of 8 channels; each thread keeps Welford's running mean and
-//     sum of squared deviations (M2) in FP32 for its 8 channels over its rows
-//     of the chunk, the block merges its row lanes with Chan's pairwise formula
+//     to 256 groups of 8 channels; each thread sums d and d^2 in FP32 for its 8
+//     channels over its rows of the chunk, d = x minus the thread's first value
+//     of the channel (a shift inside the data), turns the sums into (count,
+//     mean, M2) once, the block merges its row lanes with Chan's pairwise formula
 //     in a fixed tree, and writes one (count, mean, M2) per channel and chunk
 //     to the caller's workspace. A second kernel merges the chunks of each
 //     channel in a fixed order (one block per channel) and writes mean and the
@@ -22,10 +23,11 @@
 //     sqrt(var + eps) per channel (correctly rounded square root and
 //     division), one rounding per operation in that order, then
 //     round-to-nearest-even binary16.
-//   - Softmax of each row of x[rows, cols]: the row is cut into segments; one
-//     block per (row, segment) keeps an online (max m, sum s of exp(x - m)) per
-//     thread, merges the block's pairs in a fixed tree and writes them to the
-//     workspace. The second kernel has every block of a row merge the row's
+//   - Softmax of each row of x[rows, cols]: the row is cut into segments of
+//     32K elements; one block per (row, segment) keeps an online (max m, sum s
+//     of exp(x - m)) per thread, merges the block's pairs (a butterfly in each
+//     wave, then the waves in order) and writes them to the workspace. The
+//     second kernel has every block of a row merge the row's
 //     pairs in the same fixed order (so all agree on (M, S) to the bit) and
 //     write RNE16(exp(x - M) * (1 / S)) for its segment. m starts at -FLT_MAX,
 //     so -inf entries give exp = 0 without NaN; a NaN or +inf entry makes the
@@ -48,7 +50,7 @@ __device__ __forceinline__ Moments merge(Moments a, Moments b) {
     if (b.n == 0.0f) return a;
     if (a.n == 0.0f) return b;
     const float n = a.n + b.n;
-    const float fb = b.n / n;
+    const float fb = b.n * __builtin_amdgcn_rcpf(n);    // within 1 ulp: the statistics are bound-checked
     const float d = b.mean - a.mean;
     Moments r;
     r.n = n;
@@ -84,7 +86,8 @@ struct BnLayout {
     }
 };
 
-// grid (chunks, channel blocks); ws: cnt[chunks], mean[chunks][C], m2[chunks][C]
+// grid (chunks, channel blocks); ws: cnt[chunks], then mean[C][chunks], m2[C][chunks]
+// (channel-major, so the final merge reads each channel's chunks contiguously).
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void bn_partial_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                               int64_t C, int64_t ldx, int64_t rows_per_chunk,
@@ -96,45 +99,92 @@ __global__ __launch_bounds__(kThreads) void bn_partial_kernel(const uint16_t* __
     const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
     const int64_t c0 = (g0 + L.g) * VEC;
 
+    // Sums of d = x - k and of d^2 over this lane's rows, k the lane's first value of
+    // the channel (a shift inside the data keeps s2 - s1^2 / n free of large cancellation);
+    // converted once to (n, mean, M2) for Chan's merges.
     float n = 0.0f, mean[VEC], m2[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) mean[k] = m2[k] = 0.0f;
-    if (L.active) {
-        // Welford over this lane's rows, four rows' loads issued before their updates
-        int64_t r = r0 + L.rl;
-        for (; r + 3 * L.rp < r1; r += 4 * L.rp) {
-            float v[4][VEC];
+    if (L.active && r0 + L.rl < r1) {
+        float sh[VEC], s1[VEC], s2[VEC];
+        load_f16<VEC>(x + (r0 + L.rl) * ldx + c0, sh);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load_f16<VEC>(x + (r + u * L.rp) * ldx + c0, v[u]);
+        for (int k = 0; k < VEC; ++k) s1[k] = s2[k] = 0.0f;
+        n = 1.0f;
+        auto add = [&](const float (&v)[VEC]) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                n += 1.0f;
-                const float inv = 1.0f / n;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float d = v[u][k] - mean[k];
-                    mean[k] = mean[k] + d * inv;
-                    m2[k] = m2[k] + d * (v[u][k] - mean[k]);
-                }
+            for (int k = 0; k < VEC; ++k) {
+                const float d = v[k] - sh[k];
+                s1[k] = s1[k] + d;
+                s2[k] = s2[k] + d * d;
             }
+        };
+        int64_t r = r0 + L.rl + L.rp;
+        for (; r + 7 * L.rp < r1; r += 8 * L.rp) {                // eight rows' loads in flight
+            float v[8][VEC];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) load_f16<VEC>(x + (r + u * L.rp) * ldx + c0, v[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) add(v[u]);
+            n += 8.0f;
         }
         for (; r < r1; r += L.rp) {
             float v[VEC];
             load_f16<VEC>(x + r * ldx + c0, v);
+            add(v);
             n += 1.0f;
-            const float inv = 1.0f / n;
+        }
+        const float inv = 1.0f / n;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                const float d = v[k] - mean[k];
-                mean[k] = mean[k] + d * inv;
-                m2[k] = m2[k] + d * (v[k] - mean[k]);
-            }
+        for (int k = 0; k < VEC; ++k) {
+            const float q = s1[k] * inv;
+            mean[k] = sh[k] + q;
+            m2[k] = s2[k] - s1[k] * q;
         }
     }
 
-    // merge the row lanes of each channel group: a fixed binary tree over rl
+    // merge the row lanes of each channel group in a fixed order. When the block's
+    // channel groups divide a wave, a channel's lanes in one wave are lc apart: a
+    // butterfly of shuffles merges them, then the waves' results go through LDS.
+    // Otherwise a binary tree over rl in LDS.
     __shared__ float s_n[kThreads], s_mean[VEC][kThreads], s_m2[VEC][kThreads];
     const int t = int(threadIdx.x);
+    if (L.lc < 64 && (64 % L.lc) == 0) {
+        for (int off = L.lc; off < 64; off *= 2) {
+            const float on = __shfl_xor(n, off);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const Moments m = merge({n, mean[k], m2[k]}, {on, __shfl_xor(mean[k], off), __shfl_xor(m2[k], off)});
+                mean[k] = m.mean;
+                m2[k] = m.m2;
+            }
+            n = n + on;
+        }
+        const int w = t >> 6;
+        if ((t & 63) < L.lc) {                              // lane g of each wave
+            s_n[w * L.lc + L.g] = n;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) { s_mean[k][w * L.lc + L.g] = mean[k]; s_m2[k][w * L.lc + L.g] = m2[k]; }
+        }
+        __syncthreads();
+        if (t < L.lc) {
+            Moments acc[VEC];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[k] = {s_n[t], s_mean[k][t], s_m2[k][t]};
+            for (int v = 1; v < kThreads / 64; ++v) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc[k] = merge(acc[k], {s_n[v * L.lc + t], s_mean[k][v * L.lc + t], s_m2[k][v * L.lc + t]});
+            }
+            const int64_t chunks = gridDim.x;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                ws[chunks + (c0 + k) * chunks + blockIdx.x] = acc[k].mean;
+                ws[chunks + chunks * C + (c0 + k) * chunks + blockIdx.x] = acc[k].m2;
+            }
+            if (blockIdx.y == 0 && t == 0) ws[blockIdx.x] = acc[0].n;
+        }
+        return;
+    }
     s_n[t] = n;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) { s_mean[k][t] = mean[k]; s_m2[k][t] = m2[k]; }
@@ -153,12 +203,13 @@ __global__ __launch_bounds__(kThreads) void bn_partial_kernel(const uint16_t* __
         __syncthreads();
     }
     if (L.active && L.rl == 0) {
-        float* wmean = ws + gridDim.x + int64_t(blockIdx.x) * C;
-        float* wm2 = ws + gridDim.x + int64_t(gridDim.x) * C + int64_t(blockIdx.x) * C;
+        const int64_t chunks = gridDim.x;
+        float* wmean = ws + chunks;
+        float* wm2 = ws + chunks + chunks * C;
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            wmean[c0 + k] = s_mean[k][t];
-            wm2[c0 + k] = s_m2[k][t];
+            wmean[(c0 + k) * chunks + blockIdx.x] = s_mean[k][t];
+            wm2[(c0 + k) * chunks + blockIdx.x] = s_m2[k][t];
         }
         if (blockIdx.y == 0 && L.g == 0) ws[blockIdx.x] = s_n[t];
     }
@@ -169,10 +220,10 @@ __global__ __launch_bounds__(kThreads) void bn_final_kernel(const float* __restr
                                                             float* __restrict__ mean, float* __restrict__ var) {
     const int64_t c = blockIdx.x;
     const int t = int(threadIdx.x);
-    const float* wmean = ws + chunks;
-    const float* wm2 = ws + chunks + chunks * C;
+    const float* wmean = ws + chunks + c * chunks;
+    const float* wm2 = ws + chunks + chunks * C + c * chunks;
     Moments acc = {0.0f, 0.0f, 0.0f};
-    for (int64_t k = t; k < chunks; k += kThreads) acc = merge(acc, {ws[k], wmean[k * C + c], wm2[k * C + c]});
+    for (int64_t k = t; k < chunks; k += kThreads) acc = merge(acc, {ws[k], wmean[k], wm2[k]});
     __shared__ float s_n[kThreads], s_mean[kThreads], s_m2[kThreads];
     s_n[t] = acc.n; s_mean[t] = acc.mean; s_m2[t] = acc.m2;
     __syncthreads();
@@ -215,9 +266,7 @@ __global__ __launch_bounds__(kThreads) void bn_apply_kernel(const uint16_t* x, i
     }
     const int64_t r0 = int64_t(blockIdx.x) * rows_per_chunk;
     const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
-    for (int64_t r = r0 + L.rl; r < r1; r += L.rp) {
-        float v[VEC];
-        load_f16<VEC>(x + r * ldx + c0, v);
+    auto emit = [&](int64_t r, const float (&v)[VEC]) {
         uint16_t h[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
@@ -233,6 +282,19 @@ __global__ __launch_bounds__(kThreads) void bn_apply_kernel(const uint16_t* x, i
         } else {
             *mp::global(y + r * ldy + c0) = h[0];
         }
+    };
+    int64_t r = r0 + L.rl;
+    for (; r + 7 * L.rp < r1; r += 8 * L.rp) {                      // eight rows' loads in flight
+        float v[8][VEC];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load_f16<VEC>(x + (r + u * L.rp) * ldx + c0, v[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) emit(r + u * L.rp, v[u]);
+    }
+    for (; r < r1; r += L.rp) {
+        float v[VEC];
+        load_f16<VEC>(x + r * ldx + c0, v);
+        emit(r, v);
     }
 }
 
@@ -246,20 +308,20 @@ __device__ __forceinline__ MaxSum merge(MaxSum a, MaxSum b) {
     return {m, a.s * __expf(a.m - m) + b.s * __expf(b.m - m)};
 }
 
-// Merges the 256 threads' pairs in a fixed tree; every thread gets the result.
+// Merges the block's 256 pairs; every thread gets the same bits: a butterfly
+// within each wave (merge is commutative bit for bit: max and a sum of two
+// terms), then the four waves' results in a fixed order.
 __device__ __forceinline__ MaxSum block_merge(MaxSum v) {
-    __shared__ float s_m[kThreads], s_s[kThreads];
-    const int t = int(threadIdx.x);
-    s_m[t] = v.m; s_s[t] = v.s;
+#pragma unroll
+    for (int off = 32; off > 0; off /= 2)
+        v = merge(v, MaxSum{__shfl_xor(v.m, off), __shfl_xor(v.s, off)});
+    __shared__ float s_m[kThreads / 64], s_s[kThreads / 64];
+    const int w = int(threadIdx.x) >> 6;
+    if ((threadIdx.x & 63) == 0) { s_m[w] = v.m; s_s[w] = v.s; }
     __syncthreads();
-    for (int s = kThreads / 2; s > 0; s /= 2) {
-        if (t < s) {
-            const MaxSum r = merge(MaxSum{s_m[t], s_s[t]}, MaxSum{s_m[t + s], s_s[t + s]});
-            s_m[t] = r.m; s_s[t] = r.s;
-        }
-        __syncthreads();
-    }
-    const MaxSum r = {s_m[0], s_s[0]};
+    MaxSum r = {s_m[0], s_s[0]};
+#pragma unroll
+    for (int k = 1; k < kThreads / 64; ++k) r = merge(r, MaxSum{s_m[k], s_s[k]});
     __syncthreads();
     return r;
 }
@@ -288,9 +350,7 @@ __global__ __launch_bounds__(kThreads) void softmax_partial_kernel(const uint16_
     const uint16_t* xr = x + row * ldx;
     const Segment sg(cols, VEC, seg_vecs);
     MaxSum acc = {-FLT_MAX, 0.0f};
-    for (int64_t v = sg.v0 + threadIdx.x; v < sg.v1; v += kThreads) {
-        float e[VEC];
-        load_f16<VEC>(xr + v * VEC, e);
+    auto update = [&](const float (&e)[VEC]) {
         float vm = e[0];
 #pragma unroll
         for (int k = 1; k < VEC; ++k) vm = fmaxf(vm, e[k]);
@@ -300,6 +360,19 @@ __global__ __launch_bounds__(kThreads) void softmax_partial_kernel(const uint16_
         }
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc.s = acc.s + __expf(e[k] - acc.m);
+    };
+    int64_t v = sg.v0 + threadIdx.x;
+    for (; v + 3 * kThreads < sg.v1; v += 4 * kThreads) {      // four loads in flight
+        float e[4][VEC];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_f16<VEC>(xr + (v + u * kThreads) * VEC, e[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) update(e[u]);
+    }
+    for (; v < sg.v1; v += kThreads) {
+        float e[VEC];
+        load_f16<VEC>(xr + v * VEC, e);
+        update(e);
     }
     for (int64_t j = sg.tail0 + threadIdx.x; j < sg.tail1; j += kThreads) {
         const float e = mp::h2f(*mp::global(xr + j));
@@ -330,9 +403,7 @@ __global__ __launch_bounds__(kThreads) void softmax_norm_kernel(const uint16_t* 
     const uint16_t* xr = x + row * ldx;
     uint16_t* yr = y + row * ldy;
     const Segment sg(cols, VEC, seg_vecs);
-    for (int64_t v = sg.v0 + threadIdx.x; v < sg.v1; v += kThreads) {
-        float e[VEC];
-        load_f16<VEC>(xr + v * VEC, e);
+    auto emit = [&](int64_t v, const float (&e)[VEC]) {
         uint16_t h[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) h[k] = mp::f2h(__expf(e[k] - tot.m) * inv);
@@ -343,16 +414,29 @@ __global__ __launch_bounds__(kThreads) void softmax_norm_kernel(const uint16_t* 
         } else {
             *mp::global(yr + v) = h[0];
         }
+    };
+    int64_t v = sg.v0 + threadIdx.x;
+    for (; v + 3 * kThreads < sg.v1; v += 4 * kThreads) {      // four loads in flight
+        float e[4][VEC];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_f16<VEC>(xr + (v + u * kThreads) * VEC, e[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) emit(v + u * kThreads, e[u]);
+    }
+    for (; v < sg.v1; v += kThreads) {
+        float e[VEC];
+        load_f16<VEC>(xr + v * VEC, e);
+        emit(v, e);
     }
     for (int64_t j = sg.tail0 + threadIdx.x; j < sg.tail1; j += kThreads)
         *mp::global(yr + j) = mp::f2h(__expf(mp::h2f(*mp::global(xr + j)) - tot.m) * inv);
 }
 
 // ------------------------------------------------------------------ shapes
-constexpr int64_t kMaxChunks = 1024;
+constexpr int64_t kMaxChunks = 512;
 
-// Rows per chunk of the batch-norm kernels: at least four row iterations per
-// thread, at most kMaxChunks chunks.
+// Rows per chunk of the statistics kernel: at least four row iterations per
+// thread, more when there would be over kMaxChunks chunks to merge.
 int64_t bn_rows_per_chunk(int64_t rows, int64_t C, int vec) {
     const int64_t groups = C / vec > 0 ? C / vec : 1;
     const int64_t lc = groups < kThreads ? groups : kThreads;
@@ -368,7 +452,7 @@ int bn_vec(const void* x, int64_t ldx, int64_t C, const void* y = nullptr, int64
 }
 
 int64_t softmax_segments(int64_t cols) {
-    int64_t s = (cols + 8191) / 8192;
+    int64_t s = (cols + 32767) / 32768;
     return s < 1 ? 1 : (s > 1024 ? 1024 : s);
 }
 
@@ -417,7 +501,8 @@ extern "C" mp_status mp_bn_apply(const uint16_t* x, int64_t rows, int64_t channe
     if (!x || !mean || !var || !gamma || !beta || !y) return MP_ERR_INVALID_ARGUMENT;
     hipStream_t s = mp::as_stream(stream);
     const int vec = bn_vec(x, ldx, channels, y, ldy);
-    const int64_t per = bn_rows_per_chunk(rows, channels, vec);
+    const int64_t groups = channels / vec;
+    const int64_t per = 8 * (kThreads / (groups < kThreads ? groups : kThreads));   // eight rows per thread
     const dim3 grid(unsigned((rows + per - 1) / per), unsigned((channels / vec + kThreads - 1) / kThreads));
     if (vec == 8)
         bn_apply_kernel<8><<<grid, kThreads, 0, s>>>(x, rows, channels, ldx, mean, var, gamma, beta, eps, y, ldy, per);
