@@ -18,6 +18,7 @@ it. `cpu_baseline` times the CPU oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -71,9 +72,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=32, help="batch rows of the oracle's sample step")
-    p.add_argument("--unfused", action="store_true",
-                   help="GELU as separate point-wise kernels instead of in the GEMM epilogues")
-    p.add_argument("--pmc-kernel", choices=["fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad", "update", "update_nesterov",
+    p.add_argument("--gelu", choices=["saved", "recompute", "separate"], default="saved",
+                   help="saved: the forward epilogue stores GELU(Z) and GELU'(Z), the dgrad epilogue "
+                        "multiplies; recompute: the forward stores Z, the dgrad epilogue evaluates "
+                        "GELU'(Z); separate: point-wise kernels beside plain GEMMs")
+    p.add_argument("--unfused", action="store_true", help="the same as --gelu separate")
+    p.add_argument("--pmc-kernel", choices=["fwd", "fwd_act", "fwd_act_deriv", "dgrad", "dgrad_act", "dgrad_mul",
+                            "wgrad", "update", "update_nesterov",
                             "update_adagrad", "absmax", "bn_stats", "bn_apply", "softmax", "copy"],
                    help="only launch this kernel --pmc-reps times at the bench's shape (for counter passes)")
     p.add_argument("--pmc-reps", type=int, default=3)
@@ -100,7 +105,7 @@ def measured_traffic(group: str, kind: str):
 def pmc_kernel(args, mp, torch):
     """Launches one kernel kind a few times at the bench's shapes and nothing else of note."""
     n = WIDTH
-    if args.pmc_kernel in ("fwd", "fwd_act", "dgrad", "dgrad_act", "wgrad"):
+    if args.pmc_kernel in ("fwd", "fwd_act", "fwd_act_deriv", "dgrad", "dgrad_act", "dgrad_mul", "wgrad"):
         g = torch.Generator(device="cuda").manual_seed(0)
         A = torch.randn(n, n, device="cuda", generator=g).half()
         B = torch.randn(n, n, device="cuda", generator=g).half()
@@ -109,8 +114,10 @@ def pmc_kernel(args, mp, torch):
         flag = torch.zeros(1, dtype=torch.int32, device="cuda")
         f = {"fwd": lambda: mp.linear_fwd(A, B, Y=C),
              "fwd_act": lambda: mp.linear_fwd_act(mp.GELU, A, B, Z=C, H=D),
+             "fwd_act_deriv": lambda: mp.linear_fwd_act_deriv(mp.GELU, A, B, H=C, D=D),
              "dgrad": lambda: mp.linear_dgrad(A, B, dX=C),
              "dgrad_act": lambda: mp.linear_dgrad_act(mp.GELU, A, B, D, dZ=C),
+             "dgrad_mul": lambda: mp.linear_dgrad_mul(A, B, D, dZ=C),
              "wgrad": lambda: mp.linear_wgrad(A, B, dW=C, found_inf=flag)}[args.pmc_kernel]
     elif args.pmc_kernel.startswith("update"):
         N = LAYERS * n * n
@@ -160,7 +167,7 @@ def reductions(model, mp, torch) -> dict:
     calls = reduction_calls(mp, torch)
     out = {}
     for name, f in calls.items():
-        model.events = {}
+        model.start_events(10)
         for _ in range(10):
             model._t(name, f)
         torch.cuda.synchronize()
@@ -194,6 +201,7 @@ class Model:
         import numpy as np
         self.X = torch.from_numpy(w.X16.view(np.int16)).to(dev).view(f16)
         self.T = torch.from_numpy(w.T16.view(np.int16)).to(dev).view(f16)
+        # per layer: Z (last layer, recompute and separate modes) or GELU'(Z) (saved mode)
         self.Z = [torch.empty((BATCH, WIDTH), dtype=f16, device=dev) for _ in range(LAYERS)]
         self.H = [torch.empty((BATCH, WIDTH), dtype=f16, device=dev) for _ in range(LAYERS - 1)]
         self.dA = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)
@@ -204,13 +212,26 @@ class Model:
         self.plist = mp.ParamList(self.W, self.V, self.G, self.W16)
         self.hp = (w.lr, w.momentum, w.weight_decay)
         self.events = None
-        self.fused = True
+        self.gelu = "saved"
+
+    def start_events(self, pairs=128):
+        """Per-launch timing from here on. The events are created and recorded once up front,
+        so that a timed launch costs the host two event records and nothing else: a host stall
+        long enough for the GPU to drain the queue would put idle time between a pair."""
+        E = self.torch.cuda.Event
+        self.pool = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(pairs)]
+        for a, b in self.pool:
+            a.record(); b.record()
+        self.torch.cuda.synchronize()
+        self.pool.reverse()
+        self.events = {}
 
     def _t(self, kind, fn, *a, **k):
         if self.events is None:
             return fn(*a, **k)
-        E = self.torch.cuda.Event
-        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        if not self.pool:
+            self.pool.append((self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)))
+        e0, e1 = self.pool.pop()
         e0.record()
         r = fn(*a, **k)
         e1.record()
@@ -223,7 +244,10 @@ class Model:
         for l in range(LAYERS):
             if l == LAYERS - 1:
                 t("fwd", mp.linear_fwd, inp, self.W16[l], Y=self.Z[l])
-            elif self.fused:
+            elif self.gelu == "saved":
+                t("fwd_act_deriv", mp.linear_fwd_act_deriv, mp.GELU, inp, self.W16[l], H=self.H[l], D=self.Z[l])
+                inp = self.H[l]
+            elif self.gelu == "recompute":
                 t("fwd_act", mp.linear_fwd_act, mp.GELU, inp, self.W16[l], Z=self.Z[l], H=self.H[l])
                 inp = self.H[l]
             else:
@@ -237,8 +261,11 @@ class Model:
             t("wgrad", mp.linear_wgrad, dZ, prev, dW=self.G[l], found_inf=self.scaler.found_inf_ptr)
             if l == 0:
                 break
-            if self.fused:
-                # dZ_{l-1} = GELU'(Z_{l-1}) * (dZ_l . W_l) in the dgrad epilogue
+            if self.gelu == "saved":
+                # dZ_{l-1} = GELU'(Z_{l-1}) * (dZ_l . W_l), the derivative saved by the forward
+                t("dgrad_mul", mp.linear_dgrad_mul, dZ, self.W16[l], self.Z[l - 1], dZ=other)
+            elif self.gelu == "recompute":
+                # the same product with GELU'(Z_{l-1}) evaluated in the dgrad epilogue
                 t("dgrad_act", mp.linear_dgrad_act, mp.GELU, dZ, self.W16[l], self.Z[l - 1], dZ=other)
             else:
                 t("dgrad", mp.linear_dgrad, dZ, self.W16[l], dX=self.dC)
@@ -253,8 +280,9 @@ class Model:
     def kernel_ms(self):
         out = {}
         for k, evs in self.events.items():
-            d = [a.elapsed_time(b) for a, b in evs]
-            out[k] = {"launches": len(d), "avg_ms": sum(d) / len(d), "total_ms": sum(d)}
+            d = sorted(a.elapsed_time(b) for a, b in evs)
+            out[k] = {"launches": len(d), "avg_ms": sum(d) / len(d), "total_ms": sum(d),
+                      "median_ms": d[len(d) // 2], "max_ms": d[-1]}
         return out
 
 
@@ -322,7 +350,7 @@ def main():
     c = calibration_c()
     w = workloads.c4()
     model = Model(mp, torch, w, c)
-    model.fused = not args.unfused
+    model.gelu = "separate" if args.unfused else args.gelu
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -333,6 +361,7 @@ def main():
     model.events = None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gc.disable()
     t_wall = time.perf_counter()
     start.record()
     for _ in range(args.steps):
@@ -340,21 +369,24 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    gc.enable()
     ms = start.elapsed_time(end) / args.steps
 
     # Per-launch durations: the same number of steps once more, each launch between two HIP
     # events on the stream it runs on. They are kept out of the timed steps because every
     # recorded event is a queue marker of its own (~0.25 ms per step for the 76 of a step).
-    model.events = {}
+    model.start_events(80 * args.steps)
+    gc.disable()
     for _ in range(args.steps):
         model.step()
     torch.cuda.synchronize()
+    gc.enable()
     kern = model.kernel_ms()
     st = model.scaler.read()
 
     # The two-pass sweep (read-only check pass + update pass) that update-only
     # callers use when the gradients were not produced by mp_linear_wgrad.
-    model.events = {}
+    model.start_events(5)
     lr, mu, wd = model.hp
     for _ in range(5):
         model._t("sweep2", mp.step, model.plist, model.scaler, lr, mu, wd)
@@ -373,7 +405,7 @@ def main():
     for name, kind in (("nesterov", mp.NESTEROV), ("adagrad", mp.ADAGRAD)):
         # one untimed call first: it also waits for the list's descriptor upload
         mp.step_opt(vlist, model.scaler, kind, lr, mu, wd, 1e-10, flags=mp.MP_GRADS_PRECHECKED)
-        model.events = {}
+        model.start_events(5)
         for _ in range(5):
             model._t(name, mp.step_opt, vlist, model.scaler, kind, lr, mu, wd, 1e-10,
                      flags=mp.MP_GRADS_PRECHECKED)
@@ -388,7 +420,7 @@ def main():
     tl = mp.TensorList(model.W)
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     mp.absmax(tl, amax)                       # untimed: waits for the list's upload
-    model.events = {}
+    model.start_events(5)
     for _ in range(5):
         model._t("absmax", mp.absmax, tl, amax)
     torch.cuda.synchronize()
@@ -405,10 +437,11 @@ def main():
     step_flop = gemm_flop * (3 * LAYERS - 1)
     value = step_flop / (ms * 1e-3) / 1e12
     gemm = {}
-    kinds = [k for k in ("fwd_act", "fwd", "dgrad_act", "dgrad", "wgrad") if k in kern]
+    kinds = [k for k in ("fwd_act_deriv", "fwd_act", "fwd", "dgrad_mul", "dgrad_act", "dgrad", "wgrad") if k in kern]
     for k in kinds:
         tf = gemm_flop / (kern[k]["avg_ms"] * 1e-3) / 1e12
-        gemm[k] = {"avg_us": round(kern[k]["avg_ms"] * 1e3, 2), "TFLOPs": round(tf, 1),
+        gemm[k] = {"avg_us": round(kern[k]["avg_ms"] * 1e3, 2), "median_us": round(kern[k]["median_ms"] * 1e3, 2),
+                   "max_us": round(kern[k]["max_ms"] * 1e3, 2), "TFLOPs": round(tf, 1),
                    "frac": round(tf / PEAK_F16_TFLOPS, 4), "launches": kern[k]["launches"]}
     dom = max(kinds, key=lambda k: kern[k]["total_ms"])
     nparam = LAYERS * WIDTH * WIDTH
@@ -431,7 +464,9 @@ def main():
                                "FP16 storage, FP32 master + momentum, dynamic loss scale 2^16, "
                                "SGD lr 0.01 momentum 0.9",
                    "global_batch": BATCH, "params": nparam, "gemms_per_step": 3 * LAYERS - 1,
-                   "gelu": "separate point-wise kernels" if args.unfused else "in the GEMM epilogues",
+                   "gelu": {"saved": "in the GEMM epilogues, GELU'(Z) saved by the forward",
+                            "recompute": "in the GEMM epilogues, GELU'(Z) evaluated in the backward",
+                            "separate": "separate point-wise kernels"}[model.gelu],
                    "loss_multiplier_c": c},
         "roofline": {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": gemm[dom]["TFLOPs"],
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": gemm[dom]["frac"],

@@ -181,6 +181,32 @@ mp_status mp_linear_dgrad_act(mp_act kind, const uint16_t* dY, int64_t lddy, con
                               int64_t ldw, const uint16_t* Z, int64_t ldz, uint16_t* dZ,
                               int64_t lddz, int64_t M, int64_t N, int64_t K, mp_stream stream);
 
+/* Forward of an activated layer that keeps the activation's derivative instead
+ * of the pre-activation: with Z = RNE16(X . W^T) (not stored), H = act(Z) and
+ * D = RNE16(act'(Z)), both [M, N] binary16: the bits of mp_act_fwd(Z) and of
+ * mp_act_bwd(Z, 1.0), from one evaluation of the activation. The layer's
+ * backward then needs only D (mp_linear_dgrad_mul): D takes the bytes Z would.
+ * Source: as mp_linear_fwd_act (Steps 2 and 4 of the analysis page's §3.4).
+ * X: ldx >= K; W: ldw >= K; H: ldh >= N; D: ldd >= N. H and D must not overlap
+ * each other or the inputs.
+ * Errors: MP_ERR_INVALID_ARGUMENT for an unknown kind and as mp_linear_fwd. */
+mp_status mp_linear_fwd_act_deriv(mp_act kind, const uint16_t* X, int64_t ldx, const uint16_t* W,
+                                  int64_t ldw, uint16_t* H, int64_t ldh, uint16_t* D, int64_t ldd,
+                                  int64_t M, int64_t N, int64_t K, mp_stream stream);
+
+/* Activation gradient with the saved derivative:
+ * dZ[M, K] = RNE16(f32(RNE16(dY . W)) * f32(D)), one FP32 product of the
+ * binary16 dgrad output and D from mp_linear_fwd_act_deriv, rounded once (an
+ * IEEE product: signs, zeros, infinities and NaN as FP32 multiplication gives
+ * them). Against mp_linear_dgrad_act it adds the rounding of act' to binary16,
+ * so the result is within two binary16 ulps of the exact act'(Z) * RNE16(dY.W).
+ * Stays multiplied by the loss scale. dY: lddy >= N; W: ldw >= K; D: ldd >= K;
+ * dZ: lddz >= K. dZ must not overlap the inputs.
+ * Errors: as mp_linear_dgrad. */
+mp_status mp_linear_dgrad_mul(const uint16_t* dY, int64_t lddy, const uint16_t* W, int64_t ldw,
+                              const uint16_t* D, int64_t ldd, uint16_t* dZ, int64_t lddz, int64_t M,
+                              int64_t N, int64_t K, mp_stream stream);
+
 /* ------------------------------------------------------------------------
  * The optimizer sweep over a ragged list of parameter tensors.
  * Source: the analysis page, §3.4 "The Integrated Training Procedure",

@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
         L.mp_linear_wgrad.argtypes = [vp, i64, vp, i64, vp, i64, C.c_int, i64, i64, i64, vp, vp]
         L.mp_linear_fwd_act.argtypes = [C.c_int, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
         L.mp_linear_dgrad_act.argtypes = [C.c_int, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+        L.mp_linear_fwd_act_deriv.argtypes = [C.c_int, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+        L.mp_linear_dgrad_mul.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
         L.mp_param_list_create.argtypes = [vp, i32, C.POINTER(vp), vp]
         L.mp_param_list_destroy.argtypes = [vp]
         L.mp_param_list_numel.argtypes = [vp]
@@ -103,7 +105,8 @@ def lib() -> C.CDLL:
         for name in ("mp_linear_fwd", "mp_linear_dgrad", "mp_linear_wgrad", "mp_param_list_create",
                      "mp_param_list_destroy", "mp_step", "mp_scaler_init", "mp_scaler_update",
                      "mp_round_f32_to_f16", "mp_act_fwd", "mp_act_bwd", "mp_loss_softmax_ce",
-                     "mp_loss_mse", "mp_bn_stats", "mp_bn_apply", "mp_softmax"):
+                     "mp_loss_mse", "mp_bn_stats", "mp_bn_apply", "mp_softmax", "mp_linear_fwd_act_deriv",
+                     "mp_linear_dgrad_mul"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -209,6 +212,35 @@ def linear_dgrad_act(kind: int, dY: torch.Tensor, W: torch.Tensor, Z: torch.Tens
            "mp_linear_dgrad_act")
     return dZ
 
+
+
+def linear_fwd_act_deriv(kind: int, X: torch.Tensor, W: torch.Tensor, H: torch.Tensor | None = None,
+                         D: torch.Tensor | None = None, stream=None):
+    """H = act(Z) and D = RNE16(act'(Z)) with Z = RNE16(X . W^T) not stored; returns (H, D)."""
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    H = _out(H, (M, N), torch.float16, X.device)
+    D = _out(D, (M, N), torch.float16, X.device)
+    px, ldx = _mat(X, "X"); pw, ldw = _mat(W, "W"); ph, ldh = _mat(H, "H"); pd, ldd = _mat(D, "D")
+    _check(lib().mp_linear_fwd_act_deriv(int(kind), px, ldx, pw, ldw, ph, ldh, pd, ldd, M, N, K,
+                                         _stream(stream)), "mp_linear_fwd_act_deriv")
+    return H, D
+
+
+def linear_dgrad_mul(dY: torch.Tensor, W: torch.Tensor, D: torch.Tensor, dZ: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """dZ = RNE16(f32(RNE16(dY . W)) * f32(D)), D the derivative saved by linear_fwd_act_deriv."""
+    M, N = dY.shape
+    K = W.shape[1]
+    if W.shape[0] != N or tuple(D.shape) != (M, K):
+        raise ValueError("W must be [N, K] and D [M, K]")
+    dZ = _out(dZ, (M, K), torch.float16, dY.device)
+    pdy, lddy = _mat(dY, "dY"); pw, ldw = _mat(W, "W"); pd, ldd = _mat(D, "D"); pz, ldz = _mat(dZ, "dZ")
+    _check(lib().mp_linear_dgrad_mul(pdy, lddy, pw, ldw, pd, ldd, pz, ldz, M, N, K, _stream(stream)),
+           "mp_linear_dgrad_mul")
+    return dZ
 
 def linear_wgrad(dY: torch.Tensor, X: torch.Tensor, dW: torch.Tensor | None = None,
                  out_dtype=torch.float16, found_inf: torch.Tensor | None = None,

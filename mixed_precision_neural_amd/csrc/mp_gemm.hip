@@ -65,8 +65,8 @@ struct GemmArgs {
     uint32_t* flag;              // nullable: OR 1 if any binary16 output is inf/NaN
     int a_vec, b_vec;            // 16-byte global loads allowed for A / B
     int c_vec;                   // 16-byte output stores allowed (aligned base, ldc % 8 == 0 / % 4 for FP32)
-    void* C2;                    // kEpiAct: act(C) (binary16), ldc2
-    const uint16_t* Z;           // kEpiDact: saved pre-activation (binary16), ldz
+    void* C2;                    // kEpiAct: act(C); kEpiActD: act'(Z) (binary16), ldc2
+    const uint16_t* Z;           // kEpiDact: saved pre-activation; kEpiMul: saved act' (binary16), ldz
     int64_t ldc2, ldz;
     int aux_vec;                 // 16-byte access allowed for C2 / Z
     int pipe_ok;                 // operand panels under 4 GB: the buffer-load main loop applies
@@ -78,6 +78,8 @@ constexpr int kEpiF32 = 0;       // C = acc (FP32)
 constexpr int kEpiF16 = 1;       // C = RNE16(acc)
 constexpr int kEpiAct = 2;       // C = RNE16(acc), C2 = act(C)             (forward of an activated layer)
 constexpr int kEpiDact = 3;      // C = act'(Z) * RNE16(acc), rounded once  (dgrad into an activated layer)
+constexpr int kEpiActD = 4;      // Z = RNE16(acc) (not stored): C = act(Z), C2 = RNE16(act'(Z))
+constexpr int kEpiMul = 5;       // C = RNE16(RNE16(acc) * D), D = Z the stored act'  (dgrad with act' saved)
 
 __device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
 template <int CHUNKS>
@@ -480,10 +482,12 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
 }
 
 // Applies the binary16 point-wise tail of the epilogue to one output element
-// h = RNE16(acc) and stores it (z: the saved pre-activation, kEpiDact only).
+// h = RNE16(acc) and stores it (z: the saved pre-activation for kEpiDact, the
+// saved derivative for kEpiMul).
 template <int EPI, int KIND>
 __device__ __forceinline__ uint16_t epi_main(uint16_t h, uint16_t z) {
     if (EPI == kEpiDact) return mp::act_bwd1<KIND>(z, h);
+    if (EPI == kEpiMul) return mp::f2h(mp::h2f(h) * mp::h2f(z));
     return h;
 }
 __device__ __forceinline__ uint16_t half_of(const uint4& v, int e) {
@@ -605,7 +609,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
             z[q] = *reinterpret_cast<const uint4*>(g.Z + (wrow0 + piece_row(p0 + q)) * g.ldz + wcol0 +
                                                    8 * piece_chunk());
     };
-    if (EPI == kEpiDact && whole) zload(za, 0);
+    constexpr bool kLoadZ = EPI == kEpiDact || EPI == kEpiMul;
+    if (kLoadZ && whole) zload(za, 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -642,6 +647,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
                     for (int e = 0; e < 8; ++e) a[e] = mp::act_fwd1<KIND>(half_of(v, e));
                     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
                         make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+                } else if (EPI == kEpiActD) {
+                    uint16_t a[8], d[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mp::act_fwd_deriv1<KIND>(half_of(v, e), a[e], d[e]);
+                    *reinterpret_cast<uint4*>(dst) =
+                        make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
+                        make_uint4(pack2(d[0], d[1]), pack2(d[2], d[3]), pack2(d[4], d[5]), pack2(d[6], d[7]));
                 } else {
                     uint16_t d[8];
 #pragma unroll
@@ -653,10 +666,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
         };
 #pragma unroll 1
         for (int p0 = 0; p0 < kPasses; p0 += 2 * kGrp) {
-            if (EPI == kEpiDact && p0 + kGrp < kPasses) zload(zb, p0 + kGrp);
+            if (kLoadZ && p0 + kGrp < kPasses) zload(zb, p0 + kGrp);
             group(za, p0);
             if (p0 + kGrp < kPasses) {
-                if (EPI == kEpiDact && p0 + 2 * kGrp < kPasses) zload(za, p0 + 2 * kGrp);
+                if (kLoadZ && p0 + 2 * kGrp < kPasses) zload(za, p0 + 2 * kGrp);
                 group(zb, p0 + kGrp);
             }
         }
@@ -678,6 +691,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
                     } else if (EPI == kEpiAct) {
                         dst[e] = h;
                         static_cast<uint16_t*>(g.C2)[gr * g.ldc2 + gc + e] = mp::act_fwd1<KIND>(h);
+                    } else if (EPI == kEpiActD) {
+                        uint16_t a, d;
+                        mp::act_fwd_deriv1<KIND>(h, a, d);
+                        dst[e] = a;
+                        static_cast<uint16_t*>(g.C2)[gr * g.ldc2 + gc + e] = d;
                     } else {
                         dst[e] = epi_main<EPI, KIND>(h, g.Z[gr * g.ldz + gc + e]);
                     }
@@ -821,4 +839,35 @@ extern "C" mp_status mp_linear_dgrad_act(mp_act kind, const uint16_t* dY, int64_
     hipStream_t s = mp::as_stream(stream);
     if (kind == MP_ACT_RELU) return launch<true, false, kEpiDact, MP_ACT_RELU>(a, s, "mp_linear_dgrad_act");
     return launch<true, false, kEpiDact, MP_ACT_GELU>(a, s, "mp_linear_dgrad_act");
+}
+
+extern "C" mp_status mp_linear_fwd_act_deriv(mp_act kind, const uint16_t* X, int64_t ldx, const uint16_t* W,
+                                             int64_t ldw, uint16_t* H, int64_t ldh, uint16_t* D, int64_t ldd,
+                                             int64_t M, int64_t N, int64_t K, mp_stream stream) {
+    if (kind != MP_ACT_RELU && kind != MP_ACT_GELU) return MP_ERR_INVALID_ARGUMENT;
+    if (M < 0 || N < 0 || K < 0) return MP_ERR_INVALID_ARGUMENT;
+    if (M == 0 || N == 0) return MP_OK;
+    if (bad_matrix(X, M, K, ldx) || bad_matrix(W, N, K, ldw) || bad_matrix(H, M, N, ldh) ||
+        bad_matrix(D, M, N, ldd))
+        return MP_ERR_INVALID_ARGUMENT;
+    if (too_large(M, N)) return MP_ERR_INVALID_ARGUMENT;
+    GemmArgs a{X, W, H, ldx, ldw, ldh, M, N, K, nullptr, vec_ok(X, ldx), vec_ok(W, ldw),
+               out_vec_ok(H, ldh, MP_F16), D, nullptr, ldd, 0, out_vec_ok(D, ldd, MP_F16)};
+    hipStream_t s = mp::as_stream(stream);
+    if (kind == MP_ACT_RELU) return launch<true, true, kEpiActD, MP_ACT_RELU>(a, s, "mp_linear_fwd_act_deriv");
+    return launch<true, true, kEpiActD, MP_ACT_GELU>(a, s, "mp_linear_fwd_act_deriv");
+}
+
+extern "C" mp_status mp_linear_dgrad_mul(const uint16_t* dY, int64_t lddy, const uint16_t* W, int64_t ldw,
+                                         const uint16_t* D, int64_t ldd, uint16_t* dZ, int64_t lddz, int64_t M,
+                                         int64_t N, int64_t K, mp_stream stream) {
+    if (M < 0 || N < 0 || K < 0) return MP_ERR_INVALID_ARGUMENT;
+    if (M == 0 || K == 0) return MP_OK;
+    if (bad_matrix(dY, M, N, lddy) || bad_matrix(W, N, K, ldw) || bad_matrix(D, M, K, ldd) ||
+        bad_matrix(dZ, M, K, lddz))
+        return MP_ERR_INVALID_ARGUMENT;
+    if (too_large(M, K)) return MP_ERR_INVALID_ARGUMENT;
+    GemmArgs a{dY, W, dZ, lddy, ldw, lddz, M, K, N, nullptr, vec_ok(dY, lddy), vec_ok(W, ldw),
+               out_vec_ok(dZ, lddz, MP_F16), nullptr, D, 0, ldd, vec_ok(D, ldd)};
+    return launch<true, false, kEpiMul>(a, mp::as_stream(stream), "mp_linear_dgrad_mul");
 }

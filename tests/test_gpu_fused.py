@@ -9,6 +9,11 @@ mp_act_fwd, and mp_linear_dgrad_act the bits of mp_linear_dgrad followed by
 mp_act_bwd; each half is also checked against the oracle: the product within the
 binary16 GEMM tolerance (1e-2), ReLU exactly, GELU within one binary16 ulp of the
 oracle applied to the GPU's own product (two for the gradient).
+
+mp_linear_fwd_act_deriv stores act(Z) and RNE16(act'(Z)) instead of Z (the bits of mp_act_fwd
+and of mp_act_bwd(Z, 1.0)); mp_linear_dgrad_mul multiplies the binary16 dgrad product by that
+saved derivative in FP32 and rounds once, which is checked bit for bit against torch's FP32
+product rounded to half, and within two binary16 ulps of the oracle's exact gradient.
 """
 import numpy as np
 import pytest
@@ -133,6 +138,68 @@ def test_fused_direct_to_lds_ragged():
     Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
     check_fwd(mp.GELU, X, W, Xd, Wd, ref=False)
     check_dgrad(mp.GELU, dY, W, Zs, dYd, Wd, Zd, ref=False)
+
+
+def check_fwd_deriv(kind, Xd, Wd):
+    """H and D of the derivative-saving forward: the bits of act_fwd(Z) and act_bwd(Z, 1.0), Z
+    the binary16 product, and each within the activation's ulp bound of the oracle."""
+    H, D = mp.linear_fwd_act_deriv(kind, Xd, Wd)
+    Z = mp.linear_fwd(Xd, Wd)
+    ones = torch.ones_like(Z)
+    Hu, Du = mp.act_fwd(kind, Z), mp.act_bwd(kind, Z, ones)
+    torch.cuda.synchronize()
+    h, d, z = host_bits16(H), host_bits16(D), host_bits16(Z)
+    assert np.array_equal(h, host_bits16(Hu)), "H differs from act_fwd of the product"
+    assert np.array_equal(d, host_bits16(Du)), "D differs from act_bwd(Z, 1) of the product"
+    rh = act_ref(kind, z)
+    rd = act_grad_ref(kind, z, host_bits16(ones))
+    if kind == mp.RELU:
+        assert np.array_equal(h, rh) and np.array_equal(d, rd)
+    else:
+        assert within_ulp(h, rh) and within_ulp(d, rd, ulps=2)
+
+
+def check_dgrad_mul(kind, Zs, dYd, Wd, Zd):
+    """dZ = RNE16(f32(dgrad product) * f32(D)): bitwise against torch's FP32 product of the
+    same binary16 operands rounded to half (round to nearest even), and within two binary16
+    ulps of the oracle's exact act'(Z) * dgrad product (one extra rounding, of D)."""
+    Dd = mp.act_bwd(kind, Zd.contiguous(), torch.ones_like(Zd.contiguous()))
+    dZ = mp.linear_dgrad_mul(dYd, Wd, Dd)
+    dH = mp.linear_dgrad(dYd, Wd)
+    ref = (dH.float() * Dd.float()).half()
+    torch.cuda.synchronize()
+    out, r = host_bits16(dZ), host_bits16(ref)
+    nan = np.isnan(f16_values(out)) & np.isnan(f16_values(r))
+    assert np.array_equal(out[~nan], r[~nan]), "dZ differs from the FP32 product rounded to binary16"
+    ro = act_grad_ref(kind, np.ascontiguousarray(Zs), host_bits16(dH))
+    if kind == mp.RELU:
+        assert np.array_equal(f16_values(out), f16_values(ro))          # +0 and -0 compare equal
+    else:
+        assert within_ulp(out, ro, ulps=2)
+
+
+@pytest.mark.parametrize("kind", [mp.RELU, mp.GELU])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (64, 512, 256), (64, 10, 512), (300, 520, 200),
+                                   (777, 1000, 333), (2600, 3100, 96), (1280, 1024, 384)])
+def test_derivative_saving_layers(kind, M, N, K):
+    """mp_linear_fwd_act_deriv and mp_linear_dgrad_mul on small (64 x 64 tiles) and large
+    (256 x 256 tiles) grids, ragged in every dimension."""
+    require_gpu()
+    X, W, dY, Zs = inputs(M, N, K, M * 3 + N * 5 + K + kind)
+    Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
+    check_fwd_deriv(kind, Xd, Wd)
+    check_dgrad_mul(kind, Zs, dYd, Wd, Zd)
+
+
+@pytest.mark.parametrize("M,N,K", [(4100, 4352, 2176), (4096, 4096, 4096)])
+def test_derivative_saving_layers_direct_to_lds(M, N, K):
+    """GELU, on grids whose whole tiles take the direct-to-LDS loop (edge tiles the general one),
+    and the benchmark's 4096^3 layer."""
+    require_gpu()
+    X, W, dY, Zs = inputs(M, N, K, M + N + K)
+    Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
+    check_fwd_deriv(mp.GELU, Xd, Wd)
+    check_dgrad_mul(mp.GELU, Zs, dYd, Wd, Zd)
 
 
 def test_fused_argument_errors():
