@@ -1,4 +1,4 @@
-"""Generates the constants of the GELU evaluation in csrc/mp_internal.h (run by hand; prints C).
+"""Generates the constants of the GELU evaluation in csrc/mp_act.h (run by hand; prints C).
 
 GELU(x) = x Phi(x), Phi the standard normal CDF. For u = |x|:
     Phi(-u) = exp(-u^2 / 2) G(u),   G(u) = Phi(-u) exp(u^2 / 2),
