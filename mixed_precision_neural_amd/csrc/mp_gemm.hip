@@ -29,13 +29,13 @@
 //     one index column.
 // Both swizzles keep the fragment reads of the 256-wide tiles free of LDS bank
 // conflicts. Whole 256 x 256 tiles take a loop unrolled over the two LDS
-// stages, with buffer loads (scalar slab offsets) and fragment addresses that
+// stages: 8 waves of 128 x 64, two per SIMD, one of which loads the next slab
+// straight from global memory into LDS (buffer loads with scalar slab offsets)
+// while its partner only reads fragments and issues MFMAs; fragment addresses
 // are a few per-lane registers plus immediates, and an explicit instruction
-// order: in sub-step 0 every MFMA is paired with a global load, in sub-steps
-// 0-2 with the LDS reads of the next sub-step, in sub-step 3 with an LDS store
-// of the next slice, so memory traffic issues while the matrix cores run
-// instead of between their bursts. Edge tiles and small grids use a general
-// loop with clamped, zero-filled loads.
+// order puts the loads and the next sub-step's LDS reads between the MFMAs.
+// Edge tiles and small grids use a general loop with clamped, zero-filled
+// loads staged through registers.
 // Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
 // 8 XCDs) works on a compact group of tiles that share rows of A and B in its
 // own L2. Binary16 outputs are rounded into LDS and written back as whole
@@ -275,12 +275,13 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* st0, uint4
 
 // One operand's slab (ROWS index rows x 64 reduction elements) fetched by
 // buffer loads that write LDS directly: lane i of such a load stores its 16
-// bytes at the instruction's LDS address + 16 i, so each wave fills kPer whole
-// 1 KB blocks of the operand's region, and lane i of block b fetches the global
-// chunk that the fragment layout places at chunk 64 b + i (both swizzles are
-// XORs, hence their own inverses). No registers hold the slab and no LDS store
-// instructions are issued. The resource covers the operand's panel; each lane
-// keeps a fixed 32-bit byte offset per block, and the slab is a scalar offset.
+// bytes at the instruction's LDS address + 16 i, so each of the WAVES loading
+// waves fills kPer whole 1 KB blocks of the operand's region, and lane i of
+// block b fetches the global chunk that the fragment layout places at chunk
+// 64 b + i (both swizzles are XORs, hence their own inverses). No registers
+// hold the slab and no LDS store instructions are issued. The resource covers
+// the operand's panel; each lane keeps a fixed 32-bit byte offset per block,
+// and the slab is a scalar offset.
 template <int ROWS, int WAVES, bool KC>
 struct DmaLoader {
     static constexpr int kBlocks = ROWS * kRowChunks / 64;   // 1 KB blocks per slab
@@ -390,21 +391,29 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr uint32_t kAStage = BM * kRowChunks * 16;                    // bytes
     constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per sub-step
-    using LA = DmaLoader<BM, WAVES, A_KC>;
-    using LB = DmaLoader<BN, WAVES, B_KC>;
-    constexpr int kLoads = LA::kPer + LB::kPer;                          // loads per wave per slab
+    // With 8 waves, waves 0-3 (one per SIMD: a block's waves are dealt to the 4
+    // SIMDs in turn) load the slabs and waves 4-7 only compute. A loading wave
+    // stalls whenever the CU's vector-memory path is backed up; its partner's
+    // MFMAs keep the SIMD's matrix core busy meanwhile (4096^3: ~2% faster than
+    // every wave loading, and than 4 waves of 128 x 128). The loading waves run
+    // at a higher issue priority so that their loads go out as early as possible.
+    constexpr int kLoadWaves = WAVES == 8 ? 4 : WAVES;
+    using LA = DmaLoader<BM, kLoadWaves, A_KC>;
+    using LB = DmaLoader<BN, kLoadWaves, B_KC>;
+    constexpr int kLoads = LA::kPer + LB::kPer;                          // loads per loading wave per slab
     constexpr int kMfma = FM * FN;                                       // MFMAs per sub-step
     static_assert(FM == 4 && (FN == 4 || FN == 2) && WTM == 32 * FM && WTN == 32 * FN, "4 x 4 or 4 x 2 blocks per wave");
-    static_assert(kReads <= 2 * kMfma && kLoads <= kMfma, "reads and loads fit the sub-steps");
+    static_assert(kReads <= 2 * kMfma && kLoads <= 2 * kMfma, "reads and loads fit the sub-steps");
     static_assert(kAStage <= 32768 && BN * kRowChunks * 16 <= 32768, "fragment offsets must fit the LDS immediate");
     const int nk = int(g.R / kBK);
     typedef __attribute__((address_space(3))) uint8_t lds8;
     lds8* s8[2] = {(lds8*)st0, (lds8*)st1};
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    const bool loader = wave < kLoadWaves;
     LA la;
     LB lb;
-    la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, wave, lane);
-    lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, wave, lane);
+    la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, wave % kLoadWaves, lane);
+    lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, wave % kLoadWaves, lane);
     FragAddr<BM, A_KC> fa;
     FragAddr<BN, B_KC> fb;
     fa.init(wm * WTM, lane, 0);
@@ -435,15 +444,16 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
 
     half8 af[2][FM], bf[2][FN];
     // Prologue: slab 0 in stage 0.
-    fetch(0, 0);
+    if (loader) fetch(0, 0);
     wait_loads();
     __syncthreads();
 
-    // One slab in stage S; the next slab (or, after the last, a copy of it) is
-    // loaded into the other stage.
-    auto slab = [&](int kt, auto s_tag) {
+    // One slab in stage S; a loading wave (LD) loads its share of the next slab
+    // (or, after the last, a copy of it) into the other stage.
+    auto slab = [&](int kt, auto s_tag, auto ld_tag) {
         constexpr int S = decltype(s_tag)::value;
-        fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
+        constexpr bool LD = decltype(ld_tag)::value;
+        if constexpr (LD) fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
         read_frags(S, 0, af[0], bf[0]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -453,15 +463,17 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
         // Instruction order (groups are filled in program order): the first
         // fragments, then each MFMA followed by the next sub-step's fragment
         // reads (sub-steps 0-2: one after each of the first MFMAs with 16 per
-        // sub-step, spread evenly with 8) and, after every other MFMA of
-        // sub-steps 0 and 1, a load of the next slab. Waves issuing all their
-        // loads within one sub-step ask the CU's vector-memory path for about
-        // twice what it moves per cycle, and the waiting issue holds up the MFMAs.
+        // sub-step, spread evenly with 8) and, in a loading wave, loads of the
+        // next slab spread over sub-steps 0 and 1 (after every MFMA when a
+        // wave loads more blocks than a sub-step has MFMAs, else after every
+        // other one).
         __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
         for (int kk = 0; kk < 4; ++kk)
             for (int m = 0; m < kMfma; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (kk < 2 && !(m & 1) && kk * (kMfma / 2) + m / 2 < kLoads)
+                if (LD && kLoads <= kMfma && kk < 2 && !(m & 1) && kk * (kMfma / 2) + m / 2 < kLoads)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (LD && kLoads > kMfma && kk < 2 && kk * kMfma + m < kLoads)
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 const int nr = kMfma == 16 ? int(m < kReads) : (m + 1) * kReads / kMfma - m * kReads / kMfma;
                 if (kk < 3)
@@ -472,12 +484,24 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
+    using Load = std::integral_constant<bool, true>;
+    using NoLoad = std::integral_constant<bool, false>;
     // nk is even here. One loop body for every slab: after the last slab the
     // "next" load re-reads that slab into the idle stage (1/nk extra loads),
-    // which keeps the loop free of tail copies.
-    for (int kt = 0; kt < nk; kt += 2) {
-        slab(kt, C0());
-        slab(kt + 1, C1());
+    // which keeps the loop free of tail copies. Every wave passes one barrier
+    // per slab in either loop.
+    if (loader) {
+        __builtin_amdgcn_s_setprio(2);
+        for (int kt = 0; kt < nk; kt += 2) {
+            slab(kt, C0(), Load());
+            slab(kt + 1, C1(), Load());
+        }
+        __builtin_amdgcn_s_setprio(0);
+    } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+            slab(kt, C0(), NoLoad());
+            slab(kt + 1, C1(), NoLoad());
+        }
     }
 }
 
@@ -724,16 +748,11 @@ mp_status launch_cfg(GemmArgs a, hipStream_t s, const char* name) {
 
 template <bool A_KC, bool B_KC, int EPI, int KIND = 0>
 mp_status launch(GemmArgs a, hipStream_t s, const char* name) {
-    // Large outputs: 256 x 256 tiles. With both operands reduction-contiguous
-    // (the forward layers) 8 waves of 128 x 64, two per SIMD, so one wave's MFMAs
-    // run while the other waits (4096^3: ~4% faster); the other layouts measured
-    // ~1% slower that way and keep 4 waves of 128 x 128. Small outputs (where a
-    // 256 x 256 grid would leave most of the 256 CUs idle): 64 x 64.
+    // Large outputs: 256 x 256 tiles of 8 waves of 128 x 64, two per SIMD,
+    // split into loading and computing waves (reduce_tile_pipe). Small outputs
+    // (where a 256 x 256 grid would leave most of the 256 CUs idle): 64 x 64.
     const int64_t big_tiles = ((a.Mc + 255) / 256) * ((a.Nc + 255) / 256);
-    if (big_tiles >= 128) {
-        if constexpr (A_KC && B_KC) return launch_cfg<256, 256, 2, 4, A_KC, B_KC, EPI, KIND>(a, s, name);
-        else return launch_cfg<256, 256, 2, 2, A_KC, B_KC, EPI, KIND>(a, s, name);
-    }
+    if (big_tiles >= 128) return launch_cfg<256, 256, 2, 4, A_KC, B_KC, EPI, KIND>(a, s, name);
     return launch_cfg<64, 64, 2, 2, A_KC, B_KC, EPI, KIND>(a, s, name);
 }
 
