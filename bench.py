@@ -160,6 +160,63 @@ def reduction_calls(mp, torch) -> dict:
     return calls
 
 
+def c1_latency(mp, torch, workloads, steps: int = 200) -> dict:
+    """The 2-layer MLP step (256 -> 512 -> 10, batch 64, fused ReLU epilogues, flag from the
+    weight-gradient epilogues): nine launches of microsecond kernels, so the host's launch
+    cost bounds it. Timed eagerly and as replays of one captured HIP graph, `steps` each."""
+    cfg = workloads.c1()
+    f16 = torch.float16
+    S = mp.Scaler(cfg.scale, cfg.dynamic, cfg.growth_interval)
+    W = [torch.from_numpy(cfg.W1).cuda(), torch.from_numpy(cfg.W2).cuda()]
+    V = [torch.zeros_like(w) for w in W]
+    W16 = [mp.round_f32_to_f16(w) for w in W]
+    G = [torch.zeros(w.shape, dtype=f16, device="cuda") for w in W]
+    pl = mp.ParamList(W, V, G, W16)
+    import numpy as np
+    X = torch.from_numpy(cfg.X16.view(np.int16)).cuda().view(f16)
+    y = torch.from_numpy(cfg.labels).cuda()
+    Z1 = torch.empty((64, 512), dtype=f16, device="cuda")
+    H1, dZ1 = torch.empty_like(Z1), torch.empty_like(Z1)
+    Z2 = torch.empty((64, 10), dtype=f16, device="cuda")
+    dZ2 = torch.empty_like(Z2)
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def step():
+        mp.linear_fwd_act(mp.RELU, X, W16[0], Z=Z1, H=H1)
+        mp.linear_fwd(H1, W16[1], Y=Z2)
+        mp.loss_softmax_ce(Z2, y, S, loss, dZ2)
+        mp.linear_wgrad(dZ2, H1, dW=G[1], found_inf=S.found_inf_ptr)
+        mp.linear_dgrad_act(mp.RELU, dZ2, W16[1], Z1, dZ=dZ1)
+        mp.linear_wgrad(dZ1, X, dW=G[0], found_inf=S.found_inf_ptr)
+        mp.step(pl, S, cfg.lr, cfg.momentum, cfg.weight_decay, flags=mp.MP_GRADS_PRECHECKED)
+        S.update()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    for _ in range(10):
+        step()
+    eager_us = timed(step)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(10):
+        g.replay()
+    graph_us = timed(g.replay)
+    st = S.read()
+    pl.close()
+    return {"workload": "C1: 2-layer MLP 256->512->10, batch 64, ReLU, softmax-CE, static scale 1024",
+            "launches_per_step": 9, "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+            "steps": steps, "skipped_steps": st["skipped_steps"]}
+
+
 def reductions(model, mp, torch) -> dict:
     """The large reductions: HIP-event time per call over 10 calls, GB/s on the algorithmic
     bytes (statistics: 2 B per value read; normalization and softmax: 2 read + 2 written; the
@@ -432,6 +489,7 @@ def main():
     tl.close()
     del g_w, g_s, g_16
     fp32_reductions = reductions(model, mp, torch)
+    c1 = c1_latency(mp, torch, workloads)
 
     gemm_flop = 2.0 * WIDTH * WIDTH * BATCH
     step_flop = gemm_flop * (3 * LAYERS - 1)
@@ -484,6 +542,7 @@ def main():
         "mp_step_opt": variants,
         "absmax_method2": method2,
         "fp32_reductions": fp32_reductions,
+        "c1_step_latency": c1,
         "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")
                    if k in kern},
         "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},
