@@ -4,9 +4,12 @@ One step = one full training step of the 12-layer GELU MLP (width 4096, batch 40
 loss to N(0,1) targets, FP16 storage, FP32 master weights and momentum, dynamic loss
 scale starting at 2^16, SGD lr 0.01 momentum 0.9), i.e. every step of the method:
 12 forward GEMMs, the scaled loss gradient, 12 weight-gradient and 11 activation-gradient
-GEMMs, the GELU point-wise ops, the optimizer sweep (overflow check + fused update of
+GEMMs, GELU and its derivative in the forward and dgrad epilogues (--gelu chooses how), the
+optimizer sweep (overflow flag from the weight-gradient epilogues + one fused update pass over
 201,326,592 parameters) and the scaler update. Inputs are synthetic, generated from seed 0,
-and resident in HBM before the timed region starts.
+and resident in HBM before the timed region starts. After the timed steps the line also
+reports the other sweeps (Nesterov, Adagrad, two-pass), the |g| maximum, the large
+reductions at the pages' sizes and the 2-layer MLP step's latency, eager and as a HIP graph.
 
 Prints one JSON line. `value` is the GEMM throughput of the whole step (35 x 2 x 4096^3
 FLOP per step / step time). `roofline` is for the GEMM kernel with the largest share of

@@ -27,7 +27,8 @@
  *   - A zero M, N, numel or list length is a successful no-op; K = 0 (an
  *     empty reduction) writes zeros.
  *   - The caller owns every data buffer and every mp_scaler. The library
- *     owns only mp_param_list handles (created and destroyed here).
+ *     owns only mp_param_list and mp_tensor_list handles (created and
+ *     destroyed here).
  *   - Outputs must not alias inputs, except that master weights and momentum
  *     are updated in place by design.
  *   - Calls on different streams are safe when their buffers are disjoint;
