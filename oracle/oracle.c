@@ -21,6 +21,14 @@
  *   SGD update ....... pinned (worked examples and closed forms)
  *   scaler ........... pinned (closed-form traces)
  *   relu/gelu/losses . pinned (library erf/softmax, finite differences, closed forms)
+ *   Nesterov/Adagrad . pinned (exact-rational closed forms; reductions to plain SGD and to
+ *                      a sign step; fp64 bounds where a square root enters)
+ *   max|g|, S from it  pinned (numpy over the finite elements; closed forms; largest
+ *                      fitting power of two)
+ *   batch-norm stats . pinned (constant channels, arithmetic progressions, exact rationals)
+ *   normalization .... pinned (dyadic cases exact in FP32; special cases)
+ *   softmax .......... pinned (constant and two-valued rows in closed form; shift
+ *                      invariance; infinities and NaN)
  */
 #define _GNU_SOURCE
 #include "oracle.h"
