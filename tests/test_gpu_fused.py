@@ -6,14 +6,18 @@ point-wise activation, and the activation gradient through it.
 
 mp_linear_fwd_act must give the bits of mp_linear_fwd (binary16 out) followed by
 mp_act_fwd, and mp_linear_dgrad_act the bits of mp_linear_dgrad followed by
-mp_act_bwd; each half is also checked against the oracle: the product within the
-binary16 GEMM tolerance (1e-2), ReLU exactly, GELU within one binary16 ulp of the
-oracle applied to the GPU's own product (two for the gradient).
+mp_act_bwd. The point-wise ops themselves are pinned against the oracle over every
+finite binary16 input (test_gpu_aux.py). Against the oracle, which only sees the
+generated inputs: the product, and the activation (or its gradient) applied to the
+oracle's own product, within the binary16 dot-product bar (max error / max(|ref|,
+rms(ref)) <= 1e-2: the two products may round a value to neighbouring binary16 numbers
+before the activation).
 
 mp_linear_fwd_act_deriv stores act(Z) and RNE16(act'(Z)) instead of Z (the bits of mp_act_fwd
 and of mp_act_bwd(Z, 1.0)); mp_linear_dgrad_mul multiplies the binary16 dgrad product by that
 saved derivative in FP32 and rounds once, which is checked bit for bit against torch's FP32
-product rounded to half, and within two binary16 ulps of the oracle's exact gradient.
+product of the same two GPU tensors rounded to half, and against the oracle's exact
+act'(Z) * (dY . W) from the generated inputs within the same bar.
 """
 import numpy as np
 import pytest
@@ -26,14 +30,6 @@ from gpu_util import dev_f16, f16_values, host_bits16, rel_err, require_gpu
 pytestmark = pytest.mark.gpu
 
 TOL_F16 = 1e-2
-
-
-def within_ulp(got_bits, ref_bits, ulps=1):
-    g, r = f16_values(got_bits), f16_values(ref_bits)
-    tol = np.maximum(np.abs(r) * 2.0 ** -10 * ulps, 2.0 ** -24 * ulps)
-    both_nan = np.isnan(g) & np.isnan(r)
-    same_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
-    return bool(np.all(both_nan | same_inf | (np.abs(g - r) <= tol)))
 
 
 def act_ref(kind, z):
@@ -62,9 +58,9 @@ def check_fwd(kind, X, W, Xd, Wd, Z=None, H=None, ref=True):
     assert np.array_equal(z, host_bits16(Zu)), "Z differs from the unfused product"
     assert np.array_equal(h, host_bits16(Hu)), "H differs from the unfused activation"
     if ref:
-        assert rel_err(f16_values(z), oracle.linear_fwd(X, W)) <= TOL_F16
-    r = act_ref(kind, np.ascontiguousarray(z))
-    assert np.array_equal(h, r) if kind == mp.RELU else within_ulp(h, r)
+        z_o = oracle.linear_fwd(X, W, out_f16=True)
+        assert rel_err(f16_values(z), f16_values(z_o)) <= TOL_F16
+        assert rel_err(f16_values(h), f16_values(act_ref(kind, z_o))) <= TOL_F16
 
 
 def check_dgrad(kind, dY, W, Zs, dYd, Wd, Zd, dZ=None, ref=True):
@@ -79,9 +75,10 @@ def check_dgrad(kind, dY, W, Zs, dYd, Wd, Zd, dZ=None, ref=True):
                            "; ".join("z=%04x dh=%04x fused=%04x unfused=%04x" % (
                                host_bits16(Zd)[i, j], dh[i, j], out[i, j], ref_u[i, j]) for i, j in bad[:12]))
     if ref:
-        assert rel_err(f16_values(dh), oracle.linear_dgrad(dY, W)) <= TOL_F16
-    r = act_grad_ref(kind, np.ascontiguousarray(Zs), dh)
-    assert np.array_equal(out, r) if kind == mp.RELU else within_ulp(out, r, ulps=2)
+        dh_o = oracle.linear_dgrad(dY, W, out_f16=True)
+        assert rel_err(f16_values(dh), f16_values(dh_o)) <= TOL_F16
+        dz_o = act_grad_ref(kind, np.ascontiguousarray(Zs), dh_o)
+        assert rel_err(f16_values(out), f16_values(dz_o)) <= TOL_F16
 
 
 @pytest.mark.parametrize("kind", [mp.RELU, mp.GELU])
@@ -140,9 +137,9 @@ def test_fused_direct_to_lds_ragged():
     check_dgrad(mp.GELU, dY, W, Zs, dYd, Wd, Zd, ref=False)
 
 
-def check_fwd_deriv(kind, Xd, Wd):
+def check_fwd_deriv(kind, X, W, Xd, Wd, ref=True):
     """H and D of the derivative-saving forward: the bits of act_fwd(Z) and act_bwd(Z, 1.0), Z
-    the binary16 product, and each within the activation's ulp bound of the oracle."""
+    the binary16 product; against the oracle's activation of its own product."""
     H, D = mp.linear_fwd_act_deriv(kind, Xd, Wd)
     Z = mp.linear_fwd(Xd, Wd)
     ones = torch.ones_like(Z)
@@ -151,31 +148,34 @@ def check_fwd_deriv(kind, Xd, Wd):
     h, d, z = host_bits16(H), host_bits16(D), host_bits16(Z)
     assert np.array_equal(h, host_bits16(Hu)), "H differs from act_fwd of the product"
     assert np.array_equal(d, host_bits16(Du)), "D differs from act_bwd(Z, 1) of the product"
-    rh = act_ref(kind, z)
-    rd = act_grad_ref(kind, z, host_bits16(ones))
-    if kind == mp.RELU:
-        assert np.array_equal(h, rh) and np.array_equal(d, rd)
-    else:
-        assert within_ulp(h, rh) and within_ulp(d, rd, ulps=2)
+    if ref:
+        z_o = oracle.linear_fwd(X, W, out_f16=True)
+        assert rel_err(f16_values(h), f16_values(act_ref(kind, z_o))) <= TOL_F16
+        d_o = act_grad_ref(kind, z_o, np.full_like(z_o, 0x3C00))
+        if kind == mp.RELU:
+            # a step function: compared where the oracle's product is far from 0 (the two
+            # products differ by far less than 2^-8), which must be nearly every element
+            far = np.abs(f16_values(z_o)) >= 2.0 ** -8
+            assert far.mean() >= 0.99 and np.array_equal(d[far], d_o[far])
+        else:
+            assert rel_err(f16_values(d), f16_values(d_o)) <= TOL_F16
 
 
-def check_dgrad_mul(kind, Zs, dYd, Wd, Zd):
+def check_dgrad_mul(kind, dY, W, Zs, dYd, Wd, Zd, ref=True):
     """dZ = RNE16(f32(dgrad product) * f32(D)): bitwise against torch's FP32 product of the
-    same binary16 operands rounded to half (round to nearest even), and within two binary16
-    ulps of the oracle's exact act'(Z) * dgrad product (one extra rounding, of D)."""
+    same two binary16 GPU tensors rounded to half (round to nearest even); against the oracle's
+    exact act'(Z) * (dY . W) from the generated inputs."""
     Dd = mp.act_bwd(kind, Zd.contiguous(), torch.ones_like(Zd.contiguous()))
     dZ = mp.linear_dgrad_mul(dYd, Wd, Dd)
     dH = mp.linear_dgrad(dYd, Wd)
-    ref = (dH.float() * Dd.float()).half()
+    prod = (dH.float() * Dd.float()).half()
     torch.cuda.synchronize()
-    out, r = host_bits16(dZ), host_bits16(ref)
+    out, r = host_bits16(dZ), host_bits16(prod)
     nan = np.isnan(f16_values(out)) & np.isnan(f16_values(r))
     assert np.array_equal(out[~nan], r[~nan]), "dZ differs from the FP32 product rounded to binary16"
-    ro = act_grad_ref(kind, np.ascontiguousarray(Zs), host_bits16(dH))
-    if kind == mp.RELU:
-        assert np.array_equal(f16_values(out), f16_values(ro))          # +0 and -0 compare equal
-    else:
-        assert within_ulp(out, ro, ulps=2)
+    if ref:
+        dz_o = act_grad_ref(kind, np.ascontiguousarray(Zs), oracle.linear_dgrad(dY, W, out_f16=True))
+        assert rel_err(f16_values(out), f16_values(dz_o)) <= TOL_F16
 
 
 @pytest.mark.parametrize("kind", [mp.RELU, mp.GELU])
@@ -187,8 +187,8 @@ def test_derivative_saving_layers(kind, M, N, K):
     require_gpu()
     X, W, dY, Zs = inputs(M, N, K, M * 3 + N * 5 + K + kind)
     Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
-    check_fwd_deriv(kind, Xd, Wd)
-    check_dgrad_mul(kind, Zs, dYd, Wd, Zd)
+    check_fwd_deriv(kind, X, W, Xd, Wd)
+    check_dgrad_mul(kind, dY, W, Zs, dYd, Wd, Zd)
 
 
 @pytest.mark.parametrize("M,N,K", [(4100, 4352, 2176), (4096, 4096, 4096)])
@@ -198,8 +198,8 @@ def test_derivative_saving_layers_direct_to_lds(M, N, K):
     require_gpu()
     X, W, dY, Zs = inputs(M, N, K, M + N + K)
     Xd, Wd, dYd, Zd = dev_f16(X), dev_f16(W), dev_f16(dY), dev_f16(Zs)
-    check_fwd_deriv(mp.GELU, Xd, Wd)
-    check_dgrad_mul(mp.GELU, Zs, dYd, Wd, Zd)
+    check_fwd_deriv(mp.GELU, X, W, Xd, Wd, ref=False)
+    check_dgrad_mul(mp.GELU, dY, W, Zs, dYd, Wd, Zd, ref=False)
 
 
 def test_fused_argument_errors():

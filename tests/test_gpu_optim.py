@@ -240,9 +240,27 @@ def test_scaler_from_absmax_matches_oracle(amax, headroom):
     assert got["dynamic"] == 1 and got["growth_interval"] == 7
 
 
+def oracle_c1_max_grad(cfg) -> float:
+    """max |g| over the FP32 weight gradients of one unscaled C1 iteration, from the generated
+    inputs only (the weights do not change between the iterations the test makes)."""
+    W16 = [oracle.f32_to_f16(cfg.W1), oracle.f32_to_f16(cfg.W2)]
+    Z1 = oracle.linear_fwd(cfg.X16, W16[0], out_f16=True)
+    H1 = oracle.relu_fwd(Z1)
+    Z2 = oracle.linear_fwd(H1, W16[1], out_f16=True)
+    _, dZ2 = oracle.softmax_ce(Z2, cfg.labels, 1.0)
+    G1 = oracle.linear_wgrad(dZ2, H1)
+    dZ1 = oracle.relu_bwd(Z1, oracle.linear_dgrad(dZ2, W16[1], out_f16=True))
+    G0 = oracle.linear_wgrad(dZ1, cfg.X16)
+    m, bad = oracle.absmax([G0, G1])
+    assert bad == 0
+    return m
+
+
 def test_method2_end_to_end_on_c1():
     """The page's recipe on the two-layer model: FP32 weight gradients of a few iterations ->
-    running max|g| -> S; the same S from the oracle over the same gradients; and a loss-scaled
+    running max|g| -> S. The oracle computes its own gradients from the generated inputs: the
+    GPU's maximum is within 1e-3 of the oracle's (the products round differently), and S is the
+    oracle's (its maximum lies 16 % below the next power-of-two boundary of S). A loss-scaled
     step with that S does not overflow."""
     require_gpu()
     cfg = workloads.c1()
@@ -257,7 +275,6 @@ def test_method2_end_to_end_on_c1():
     loss = torch.empty(1, dtype=torch.float32, device="cuda")
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     tl = mp.TensorList(G)
-    host_grads = []
     for it in range(3):
         mp.linear_fwd_act(mp.RELU, X, W16[0], Z=Z1, H=H1)
         mp.linear_fwd(H1, W16[1], Y=Z2)
@@ -266,11 +283,10 @@ def test_method2_end_to_end_on_c1():
         mp.linear_dgrad_act(mp.RELU, dZ2, W16[1], Z1, dZ=dZ1)
         mp.linear_wgrad(dZ1, X, dW=G[0], out_dtype=torch.float32)
         mp.absmax(tl, amax)
-        host_grads += [host_f32(g).copy() for g in G]
     S = mp.Scaler(1.0, False)
     mp.scaler_init_from_absmax(S, amax, 2.0)
-    ref_max, _ = oracle.absmax(host_grads)
-    assert float(amax.item()) == ref_max
+    ref_max = oracle_c1_max_grad(cfg)
+    assert abs(float(amax.item()) - ref_max) <= 1e-3 * ref_max
     scale = S.read()["scale"]
     assert scale == oracle.scale_from_absmax(ref_max, 2.0) and scale > 1.0
     # the scaled binary16 weight gradients of the same iteration stay finite
