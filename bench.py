@@ -394,7 +394,7 @@ def cpu_baseline(w, c, rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

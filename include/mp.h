@@ -48,7 +48,7 @@ typedef enum {
     MP_OK = 0,
     MP_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad leading dim, bad scale */
     MP_ERR_MISALIGNED = 2,         /* reserved: every entry point has an unaligned path      */
-    MP_ERR_UNSUPPORTED = 3,        /* a flag or dtype this build does not implement          */
+    MP_ERR_UNSUPPORTED = 3,        /* a flag or dtype that is not implemented                 */
     MP_ERR_HIP = 4,                /* a HIP runtime call failed; see mp_last_hip_error()     */
     MP_ERR_OUT_OF_MEMORY = 5       /* allocation of a library-owned handle failed            */
 } mp_status;
