@@ -18,9 +18,13 @@ import re
 import torch
 
 __all__ = [
-    "MPError", "lib", "linear_fwd", "linear_dgrad", "linear_wgrad", "ParamList", "step",
-    "Scaler", "round_f32_to_f16", "act_fwd", "act_bwd", "loss_softmax_ce", "loss_mse",
-    "MP_GRADS_PRECHECKED", "RELU", "GELU", "LIB_PATH", "HEADER_PATH",
+    "MPError", "lib", "header_functions", "LIB_PATH", "HEADER_PATH",
+    "linear_fwd", "linear_dgrad", "linear_wgrad", "linear_fwd_act", "linear_dgrad_act",
+    "linear_fwd_act_deriv", "linear_dgrad_mul",
+    "Scaler", "ParamList", "step", "step_opt", "TensorList", "absmax", "scaler_init_from_absmax",
+    "round_f32_to_f16", "act_fwd", "act_bwd", "loss_softmax_ce", "loss_mse",
+    "bn_stats", "bn_apply", "softmax",
+    "MP_GRADS_PRECHECKED", "RELU", "GELU", "SGD", "NESTEROV", "ADAGRAD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
