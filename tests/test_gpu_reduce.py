@@ -96,6 +96,20 @@ def test_bn_stats_strided_and_constant():
         assert gm[3] == 2.5 and gv[3] == 0.0
 
 
+def test_bn_stats_very_wide_pitch():
+    """A row pitch of 2^20 values (2 MiB between rows; a chunk of rows spans over 2^31 bytes):
+    the 16-byte path's addressing at pitches far beyond the channel count."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = normal_f16(rng, (120, 40), mean_scale=1.0)
+    mean, var = mp.bn_stats(padded(x, 1 << 20))
+    torch.cuda.synchronize()
+    gm, gv = host_f32(mean).astype(np.float64), host_f32(var).astype(np.float64)
+    rm, rv = oracle.bn_stats(x)
+    assert np.all(np.abs(gm - rm) <= 1e-5 * np.sqrt(rv) + 1e-6 * np.abs(rm) + 1e-30)
+    assert np.all(np.abs(gv - rv) <= 5e-5 * rv + 1e-6 * rm * rm + 1e-30)
+
+
 # ---------------------------------------------------------------- normalization
 @pytest.mark.parametrize("rows,ch", [(37, 5), (1000, 64), (4099, 72), (513, 260), (401408, 64)])
 def test_bn_apply_bit_exact(rows, ch):
