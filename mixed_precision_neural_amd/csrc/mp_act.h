@@ -77,5 +77,22 @@ __device__ __forceinline__ void act_fwd_deriv1(uint16_t xh, uint16_t& a, uint16_
     a = f2h(gelu_f(n, x));
     d = f2h(1.0f * gelu_d(n, x));
 }
+// act_fwd_deriv1 of two values, packed: a01 = act(x0) | act(x1) << 16, d01 the
+// same for act'; the same bits, with one packed conversion per pair.
+template <int KIND>
+__device__ __forceinline__ void act_fwd_deriv2(uint16_t x0, uint16_t x1, uint32_t& a01, uint32_t& d01) {
+    if (KIND == 0) {
+        uint16_t a0, d0, a1, d1;
+        act_fwd_deriv1<0>(x0, a0, d0);
+        act_fwd_deriv1<0>(x1, a1, d1);
+        a01 = uint32_t(a0) | uint32_t(a1) << 16;
+        d01 = uint32_t(d0) | uint32_t(d1) << 16;
+        return;
+    }
+    const float y0 = h2f(x0), y1 = h2f(x1);
+    const NormalCdf n0 = std_normal(y0), n1 = std_normal(y1);
+    a01 = f2h2(gelu_f(n0, y0), gelu_f(n1, y1));
+    d01 = f2h2(1.0f * gelu_d(n0, y0), 1.0f * gelu_d(n1, y1));
+}
 
 }  // namespace mp

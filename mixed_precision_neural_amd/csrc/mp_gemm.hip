@@ -643,9 +643,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
             for (int q = 0; q < 4; ++q) {
                 const int m = i * 32 + (lane & 31);
                 const int c = (j * 32 + 8 * q) / 8;            // chunk of the 8 columns 32 j + 8 q ..
-                const uint32_t h0 = mp::f2h(acc[i][j][4 * q]), h1 = mp::f2h(acc[i][j][4 * q + 1]);
-                const uint32_t h2 = mp::f2h(acc[i][j][4 * q + 2]), h3 = mp::f2h(acc[i][j][4 * q + 3]);
-                const uint2 v = make_uint2(h0 | h1 << 16, h2 | h3 << 16);
+                const uint2 v = make_uint2(mp::f2h2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                           mp::f2h2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
                 *reinterpret_cast<uint2*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16 +
                                           8 * (lane >> 5)) = v;
             }
@@ -672,13 +671,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
                     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
                         make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
                 } else if (EPI == kEpiActD) {
-                    uint16_t a[8], d[8];
+                    uint32_t a[4], d[4];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) mp::act_fwd_deriv1<KIND>(half_of(v, e), a[e], d[e]);
-                    *reinterpret_cast<uint4*>(dst) =
-                        make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+                    for (int e = 0; e < 4; ++e)
+                        mp::act_fwd_deriv2<KIND>(half_of(v, 2 * e), half_of(v, 2 * e + 1), a[e], d[e]);
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(a[0], a[1], a[2], a[3]);
                     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C2) + gr * g.ldc2 + gc) =
-                        make_uint4(pack2(d[0], d[1]), pack2(d[2], d[3]), pack2(d[4], d[5]), pack2(d[6], d[7]));
+                        make_uint4(d[0], d[1], d[2], d[3]);
                 } else {
                     uint16_t d[8];
 #pragma unroll

@@ -52,6 +52,15 @@ __device__ __forceinline__ uint16_t f2h(float f) {
     _Float16 x = static_cast<_Float16>(f);
     return __builtin_bit_cast(uint16_t, x);
 }
+// Two values at once, a in the low half: one v_cvt_pk_f16_f32, the same
+// rounding per element as f2h (both inputs pinned the same way).
+__device__ __forceinline__ uint32_t f2h2(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    asm("" : "+v"(a));
+    asm("" : "+v"(b));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
 // 1 when either binary16 half of the word has an all-ones exponent (inf/NaN).
 __device__ __forceinline__ uint32_t nonfinite2(uint32_t w) {
     return ((w & 0x7C00u) == 0x7C00u) | ((w & 0x7C000000u) == 0x7C000000u);
