@@ -37,14 +37,14 @@ __device__ __forceinline__ float horner(float z, const float (&c)[N]) {
 __device__ __forceinline__ NormalCdf std_normal(float x) {
     const float u = fminf(fabsf(x), kGeluU);
     const float e = __builtin_amdgcn_exp2f(kGeluE * (x * x));
-    const float s = __builtin_amdgcn_rcpf(1.0f + kGeluP * u);
+    const float s = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluP, u, 1.0f));
     const float z = __builtin_fmaf(s, kGeluA, kGeluB);
     const float q = e * horner(z, kGeluC8);          // Phi(-|x|)
     return {x < 0.0f ? q : 1.0f - q, e};
 }
 __device__ __forceinline__ float gelu_f(const NormalCdf& n, float x) { return x * n.cdf; }
 __device__ __forceinline__ float gelu_d(const NormalCdf& n, float x) {
-    return n.cdf + (x * 0.39894228040143267794f) * n.e;
+    return __builtin_fmaf(x * 0.39894228040143267794f, n.e, n.cdf);
 }
 // kind: 0 = ReLU, 1 = GELU (the values of mp_act)
 template <int KIND>
