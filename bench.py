@@ -51,14 +51,14 @@ MEASURED_TRAFFIC = {
              "dgrad_act": (114874.2, 32768.0), "dgrad_mul": (114802.7, 32768.0), "wgrad": (98418.7, 32768.0)},
     "update": {"src": ["mp_step.hip", "mp_internal.h"],
                "sha256": "89349111a21808b58ff0e968c243bceb0bba8d35a1d9f0a64307219cc2cb5838",
-               "update": (990915.7, 1972313.3), "nesterov": (990269.7, 1973206.9),
-               "adagrad": (993422.0, 1969809.2)},
+               "update": (991013.1, 1972320.5), "nesterov": (990377.4, 1973136.1),
+               "adagrad": (993657.8, 1969755.7)},
     "reduce": {"src": ["mp_reduce.hip", "mp_internal.h"],
-               "sha256": "de05960c50b5d36837c0885b2466889d9cb35d2329aac6094a1850d31eaed19a",
-               "bn_stats": (25338.2, 2021.7), "bn_apply": (25147.2, 50176.0), "softmax": (99258.6, 99198.0)},
+               "sha256": "155ad0ce75ce117147f5db8bd3ec51a2dbedf67916ed9d698ba6df338ebdc8a2",
+               "bn_stats": (25345.7, 2021.7), "bn_apply": (25147.4, 50176.0), "softmax": (99254.1, 99198.0)},
     "stats": {"src": ["mp_stats.hip", "mp_internal.h"],
               "sha256": "c1702f46e8f4692c3e5763ecf2e69aae3a2535bdecd36abd1217e95bfdd28f18",
-              "absmax": (394786.5, 7.6)},
+              "absmax": (394786.6, 7.5)},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # The large reductions at the pages' sizes: batch normalization over 32 images x 112 x 112

@@ -215,28 +215,35 @@ __global__ __launch_bounds__(kThreads) void bn_partial_kernel(const uint16_t* __
     }
 }
 
-// One block per channel: merges the chunks' moments in a fixed order.
-__global__ __launch_bounds__(kThreads) void bn_final_kernel(const float* __restrict__ ws, int64_t chunks, int64_t C,
-                                                            float* __restrict__ mean, float* __restrict__ var) {
+// One wave per channel: merges the chunks' moments in a fixed order. Lane t takes
+// chunks t, t + 64, ... (up to eight, all loaded before the first merge; more only
+// past kMaxChunks chunks), then a butterfly of shuffles merges the lanes; lane 0's
+// result is stored.
+__global__ __launch_bounds__(64) void bn_final_kernel(const float* __restrict__ ws, int64_t chunks, int64_t C,
+                                                      float* __restrict__ mean, float* __restrict__ var) {
     const int64_t c = blockIdx.x;
     const int t = int(threadIdx.x);
     const float* wmean = ws + chunks + c * chunks;
     const float* wm2 = ws + chunks + chunks * C + c * chunks;
-    Moments acc = {0.0f, 0.0f, 0.0f};
-    for (int64_t k = t; k < chunks; k += kThreads) acc = merge(acc, {ws[k], wmean[k], wm2[k]});
-    __shared__ float s_n[kThreads], s_mean[kThreads], s_m2[kThreads];
-    s_n[t] = acc.n; s_mean[t] = acc.mean; s_m2[t] = acc.m2;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s /= 2) {
-        if (t < s) {
-            const Moments m = merge({s_n[t], s_mean[t], s_m2[t]}, {s_n[t + s], s_mean[t + s], s_m2[t + s]});
-            s_n[t] = m.n; s_mean[t] = m.mean; s_m2[t] = m.m2;
-        }
-        __syncthreads();
+    Moments m[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {                       // a lane past the end reloads the last chunk
+        const int64_t k = t + 64 * u < chunks ? t + 64 * u : chunks - 1;
+        m[u] = {ws[k], wmean[k], wm2[k]};
     }
+    __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the merges
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (t + 64 * u >= chunks) m[u] = {0.0f, 0.0f, 0.0f};   // and contributes nothing
+    Moments acc = m[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) acc = merge(acc, m[u]);
+    for (int64_t k = t + 512; k < chunks; k += 64) acc = merge(acc, {ws[k], wmean[k], wm2[k]});
+    for (int off = 32; off > 0; off >>= 1)
+        acc = merge(acc, {__shfl_xor(acc.n, off), __shfl_xor(acc.mean, off), __shfl_xor(acc.m2, off)});
     if (t == 0) {
-        mean[c] = s_mean[0];
-        var[c] = s_m2[0] / s_n[0];
+        mean[c] = acc.mean;
+        var[c] = acc.m2 / acc.n;
     }
 }
 
@@ -489,7 +496,7 @@ extern "C" mp_status mp_bn_stats(const uint16_t* x, int64_t rows, int64_t channe
         bn_partial_kernel<1><<<grid, kThreads, 0, s>>>(x, rows, channels, ldx, per, ws);
     mp_status st = mp::launch_status("bn_partial_kernel");
     if (st != MP_OK) return st;
-    bn_final_kernel<<<unsigned(channels), kThreads, 0, s>>>(ws, chunks, channels, mean, var);
+    bn_final_kernel<<<unsigned(channels), 64, 0, s>>>(ws, chunks, channels, mean, var);
     return mp::launch_status("bn_final_kernel");
 }
 
