@@ -50,9 +50,9 @@ MEASURED_TRAFFIC = {
              "fwd": (98406.8, 32768.0), "fwd_act": (98476.2, 65536.0), "fwd_act_deriv": (98483.2, 65536.0),
              "dgrad_act": (114874.2, 32768.0), "dgrad_mul": (114802.7, 32768.0), "wgrad": (98418.7, 32768.0)},
     "update": {"src": ["mp_step.hip", "mp_internal.h"],
-               "sha256": "89349111a21808b58ff0e968c243bceb0bba8d35a1d9f0a64307219cc2cb5838",
-               "update": (991013.1, 1972320.5), "nesterov": (990377.4, 1973136.1),
-               "adagrad": (993657.8, 1969755.7)},
+               "sha256": "e5ea3aff9795752032a623271d7738611019a843dd1fa5fd24887479ee853aeb",
+               "update": (990844.1, 1972212.6), "nesterov": (990309.5, 1973116.0),
+               "adagrad": (993440.6, 1969707.7)},
     "reduce": {"src": ["mp_reduce.hip", "mp_internal.h"],
                "sha256": "155ad0ce75ce117147f5db8bd3ec51a2dbedf67916ed9d698ba6df338ebdc8a2",
                "bn_stats": (25345.7, 2021.7), "bn_apply": (25147.4, 50176.0), "softmax": (99254.1, 99198.0)},
@@ -198,11 +198,12 @@ def c1_latency(mp, torch, workloads, steps: int = 200) -> dict:
     Z2 = torch.empty((64, 10), dtype=f16, device="cuda")
     dZ2 = torch.empty_like(Z2)
     loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mp.loss_softmax_ce_workspace(64, 10), dtype=torch.uint8, device="cuda")
 
     def step():
         mp.linear_fwd_act(mp.RELU, X, W16[0], Z=Z1, H=H1)
         mp.linear_fwd(H1, W16[1], Y=Z2)
-        mp.loss_softmax_ce(Z2, y, S, loss, dZ2)
+        mp.loss_softmax_ce(Z2, y, S, loss, dZ2, workspace=ws)
         mp.linear_wgrad(dZ2, H1, dW=G[1], found_inf=S.found_inf_ptr)
         mp.linear_dgrad_act(mp.RELU, dZ2, W16[1], Z1, dZ=dZ1)
         mp.linear_wgrad(dZ1, X, dW=G[0], found_inf=S.found_inf_ptr)
@@ -260,6 +261,237 @@ def reductions(model, mp, torch) -> dict:
     return out
 
 
+def _event_avg_ms(torch, fn, reps: int, before=None) -> float:
+    """Mean of `reps` launches of fn, each between two HIP events on the current stream (the
+    stream the kernels run on); `before` runs untimed ahead of each launch."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        if before is not None:
+            before()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / reps
+
+
+def hbm_ceiling(torch, probe, gib: int = 4) -> dict:
+    """Achievable HBM rates over `gib` GiB with the stream probe (read only, write only, 1:1 copy),
+    the best of eight launch shapes each (one block per 16 KiB or 1024-4096 persistent blocks;
+    temporal or non-temporal accesses), 5 timed launches per shape."""
+    nbytes = gib << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for mode, name, moved in ((probe.READ, "read", nbytes), (probe.WRITE, "write", nbytes),
+                              (probe.COPY, "copy", 2 * nbytes)):
+        best = None
+        for blocks in (0, 1024, 2048, 4096):
+            for nt in (False, True):
+                f = lambda: probe.hbm(mode, src, dst, nbytes, blocks, nt)
+                f()
+                ms = _event_avg_ms(torch, f, 5)
+                gbps = moved / (ms * 1e-3) / 1e9
+                if best is None or gbps > best[0]:
+                    best = (gbps, blocks, nt, ms)
+        out[name] = {"GBps": round(best[0], 1), "frac": round(best[0] / PEAK_HBM_GBPS, 4),
+                     "blocks": best[1] or "one per 16 KiB", "nontemporal": best[2],
+                     "us": round(best[3] * 1e3, 1)}
+    out["bytes"] = nbytes
+    del src, dst
+    return out
+
+
+def mfma_clock(torch, probe, blocks: int = 256, ms_target: float = 25.0) -> dict:
+    """The shader clock under a binary16 matrix-core load (one block of four waves per CU, eight
+    independent v_mfma_f32_32x32x16_f16 chains per wave) and the MFMA rate it reaches."""
+    out_t = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda")
+    iters = 2000
+    probe.mfma_clock(blocks, iters, out_t)                 # warm-up and sizing
+    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t), 1)
+    iters = max(2000, int(iters * ms_target / max(ms, 1e-3)))
+    khz = probe.mfma_clock(blocks, iters, out_t)
+    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t), 1)
+    t = out_t.cpu().numpy().reshape(blocks, 4).astype("float64")
+    mhz = (t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2]) * khz / 1000.0
+    flop = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    tf = flop / (ms * 1e-3) / 1e12
+    mhz_med = float(sorted(mhz)[len(mhz) // 2])
+    return {"clock_mhz": round(mhz_med, 1), "clock_mhz_min": round(float(mhz.min()), 1),
+            "mfma_f16_TFLOPs": round(tf, 1), "frac_of_spec": round(tf / PEAK_F16_TFLOPS, 4),
+            "clock_adjusted_peak_TFLOPs": round(PEAK_F16_TFLOPS * mhz_med / 2400.0, 1),
+            "kernel_ms": round(ms, 3), "realtime_khz": khz,
+            "load": f"{blocks} blocks x 4 waves, 8 independent MFMA chains per wave, {iters} rounds"}
+
+
+def sweep_config(mp, torch, name, tensors, scale, hyper, inject, reps, copy_gbps) -> dict:
+    """The optimizer sweep over `tensors` (list of (w32, v32, g16, w16)) timed four ways: the two-
+    pass step update-only callers use (check pass + update pass), the single update pass
+    (MP_GRADS_PRECHECKED), the check pass alone (MP_CHECK_ONLY), and a step whose gradients hold
+    the injected non-finite values (the check finds them, the update pass leaves at once)."""
+    W, V, G, H = (list(x) for x in zip(*tensors))
+    n = sum(w.numel() for w in W)
+    pl = mp.ParamList(W, V, G, H)
+    S = mp.Scaler(scale, True, 2000)
+    lr, mu, wd = hyper
+    mp.step(pl, S, lr, mu, wd)                            # untimed: waits for the list's upload
+    S.update()
+    two = _event_avg_ms(torch, lambda: mp.step(pl, S, lr, mu, wd), reps)
+    one = _event_avg_ms(torch, lambda: mp.step(pl, S, lr, mu, wd, flags=mp.MP_GRADS_PRECHECKED), reps)
+    chk = _event_avg_ms(torch, lambda: mp.step(pl, S, lr, mu, wd, flags=mp.MP_CHECK_ONLY), reps)
+    restore = inject()
+    reset = lambda: S.init(scale, True, 2000)
+    skip = _event_avg_ms(torch, lambda: mp.step(pl, S, lr, mu, wd), reps, before=reset)
+    st = S.read()
+    restore()
+    pl.close()
+    alg = SWEEP_BYTES_PER_PARAM * n
+    gb = lambda ms: alg / (ms * 1e-3) / 1e9
+    return {"workload": name, "params": n, "tensors": len(W), "algorithmic_bytes": alg,
+            "two_pass_us": round(two * 1e3, 1), "two_pass_GBps": round(gb(two), 1),
+            "two_pass_frac": round(gb(two) / PEAK_HBM_GBPS, 4),
+            "one_pass_us": round(one * 1e3, 1), "one_pass_GBps": round(gb(one), 1),
+            "one_pass_frac": round(gb(one) / PEAK_HBM_GBPS, 4),
+            "one_pass_frac_of_copy_ceiling": round(gb(one) / copy_gbps, 4) if copy_gbps else None,
+            "check_only_us": round(chk * 1e3, 1),
+            "check_only_GBps": round(CHECK_BYTES_PER_PARAM * n / (chk * 1e-3) / 1e9, 1),
+            "skipped_step_us": round(skip * 1e3, 1), "skipped_flag": st["found_inf"]}
+
+
+def c2_sweep(mp, torch, copy_gbps, reps=10, n=100_000_000) -> dict:
+    """C2: one flat tensor of 10^8 parameters; w ~ N(0, 0.02^2), v = 0, g = RNE16(2^15 * sign *
+    2^U(-34, -4)); +inf at one seeded index for the skipped step. Drawn on the GPU (the same
+    distributions as the parity inputs; timing does not depend on the draw)."""
+    g = torch.Generator(device="cuda").manual_seed(2)
+    w = torch.randn(n, device="cuda", generator=g) * 0.02
+    v = torch.zeros(n, device="cuda")
+    u = torch.rand(n, device="cuda", generator=g) * 30.0 - 34.0
+    sign = torch.randint(0, 2, (n,), device="cuda", generator=g).float() * 2 - 1
+    g16 = (sign * torch.exp2(u) * 2.0 ** 15).half()
+    del u, sign
+    h = torch.empty(n, dtype=torch.float16, device="cuda")
+    idx = int(torch.randint(0, n, (1,), generator=torch.Generator().manual_seed(25)))
+
+    def inject():
+        old = g16[idx].clone()
+        g16[idx] = float("inf")
+        return lambda: g16[idx].copy_(old)
+    out = sweep_config(mp, torch, "C2: one tensor of 10^8 parameters, SGD lr 0.01 momentum 0.9, S = 2^15",
+                       [(w, v, g16, h)], 2.0 ** 15, (0.01, 0.9, 0.0), inject, reps, copy_gbps)
+    out["_host"] = (w, v, g16, h)
+    return out
+
+
+def c5_sweep(mp, torch, workloads, copy_gbps, reps=5) -> dict:
+    """C5: 500 ragged tensors (log-uniform sizes rescaled to 1.5e9 parameters), w ~ N(0, 0.02^2),
+    v = 0, log2|g| ~ N(-20, 2.43^2) times S = 2^12, 0.1 % NaN for the skipped step; SGD lr 1e-3
+    momentum 0.9 weight decay 1e-4. Drawn on the GPU per tensor."""
+    sizes = workloads.c5_sizes()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    tensors = []
+    for sz in sizes.tolist():
+        w = torch.randn(sz, device="cuda", generator=g) * 0.02
+        e = torch.randn(sz, device="cuda", generator=g) * workloads.C5_LOG2_SIGMA + workloads.C5_LOG2_MEDIAN
+        sign = torch.randint(0, 2, (sz,), device="cuda", generator=g).float() * 2 - 1
+        g16 = (sign * torch.exp2(e) * 2.0 ** 12).half()
+        del e, sign
+        tensors.append((w, torch.zeros_like(w), g16, torch.empty(sz, dtype=torch.float16, device="cuda")))
+    torch.cuda.synchronize()
+
+    def inject():
+        saved = []
+        for (_, _, g16, _) in tensors:
+            m = torch.rand(g16.numel(), device="cuda", generator=g) < 1e-3
+            saved.append((g16, m, g16[m].clone()))
+            g16[m] = float("nan")
+
+        def restore():
+            for g16, m, old in saved:
+                g16[m] = old
+        return restore
+    out = sweep_config(mp, torch, "C5: 500 ragged tensors, 1.5e9 parameters, SGD lr 1e-3 momentum 0.9 "
+                       "weight decay 1e-4, S = 2^12", tensors, 2.0 ** 12, (1e-3, 0.9, 1e-4), inject, reps,
+                       copy_gbps)
+    out["_host"] = tensors
+    return out
+
+
+def c3_gemms(mp, torch, reps=10, M=8192, N=4096, K=4096) -> dict:
+    """C3: one linear layer of 8192 tokens, 4096 -> 4096: forward, dgrad and wgrad with binary16
+    outputs, each over `reps` launches after two untimed ones. X, dY ~ N(0,1), W ~ N(0, 1/64^2)."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    X = torch.randn(M, K, device="cuda", generator=g).half()
+    dY = torch.randn(M, N, device="cuda", generator=g).half()
+    W = (torch.randn(N, K, device="cuda", generator=g) / 64.0).half()
+    Y = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.float16, device="cuda")
+    dW = torch.empty(N, K, dtype=torch.float16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    calls = {"fwd": lambda: mp.linear_fwd(X, W, Y=Y), "dgrad": lambda: mp.linear_dgrad(dY, W, dX=dX),
+             "wgrad": lambda: mp.linear_wgrad(dY, X, dW=dW, found_inf=flag)}
+    flop = 2.0 * M * N * K
+    out = {"workload": f"C3: M={M} tokens, N={N}, K={K}, binary16 in and out, FP32 accumulation",
+           "gflop_per_launch": round(flop / 1e9, 2)}
+    for k, f in calls.items():
+        f(); f()
+        ms = _event_avg_ms(torch, f, reps)
+        tf = flop / (ms * 1e-3) / 1e12
+        out[k] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_F16_TFLOPS, 4)}
+    out["_host"] = (X, dY, W)
+    return out
+
+
+def cpu_configs(c2, c3, c5) -> dict:
+    """The oracle on bounded samples of C2, C3 and C5 (CPU threads of the host)."""
+    import numpy as np
+
+    import oracle
+    res = {}
+    w, v, g16, h = c2.pop("_host")
+    hw, hv = w.cpu().numpy().copy(), v.cpu().numpy().copy()
+    hg = g16.cpu().numpy().view(np.uint16).copy()
+    hh = h.cpu().numpy().view(np.uint16).copy()
+    t0 = time.perf_counter()
+    oracle.step([hw], [hv], [hg], [hh], 0.01, 0.9, 0.0, 2.0 ** -15)
+    dt = time.perf_counter() - t0
+    res["c2"] = {"sample": "the full C2 step (two passes: check, then update) over 10^8 parameters",
+                 "seconds": round(dt, 3), "GBps": round(SWEEP_BYTES_PER_PARAM * hw.size / dt / 1e9, 2)}
+    del hw, hv, hg, hh
+    tensors = c5.pop("_host")
+    sel, total = [], 0
+    for t in tensors:
+        if total >= 100_000_000:
+            break
+        sel.append(t); total += t[0].numel()
+    hw = [t[0].cpu().numpy().copy() for t in sel]
+    hv = [t[1].cpu().numpy().copy() for t in sel]
+    hg = [t[2].cpu().numpy().view(np.uint16).copy() for t in sel]
+    hh = [np.zeros(t[0].numel(), np.uint16) for t in sel]
+    t0 = time.perf_counter()
+    oracle.step(hw, hv, hg, hh, 1e-3, 0.9, 1e-4, 2.0 ** -12)
+    dt = time.perf_counter() - t0
+    res["c5"] = {"sample": f"the C5 step over its first {len(sel)} tensors ({total} parameters)",
+                 "seconds": round(dt, 3), "GBps": round(SWEEP_BYTES_PER_PARAM * total / dt / 1e9, 2)}
+    del hw, hv, hg, hh
+    X, dY, W = (np.ascontiguousarray(t.cpu().numpy().view(np.uint16)) for t in c3.pop("_host"))
+    rows = 16
+    t0 = time.perf_counter(); oracle.linear_fwd(X[:rows], W, out_f16=True); t_f = time.perf_counter() - t0
+    t0 = time.perf_counter(); oracle.linear_dgrad(dY[:rows], W, out_f16=True); t_d = time.perf_counter() - t0
+    rng = np.random.Generator(np.random.PCG64(6))
+    pts = 32768
+    r, cc = rng.integers(0, W.shape[0], pts), rng.integers(0, W.shape[1], pts)
+    t0 = time.perf_counter(); oracle.linear_wgrad_at(dY, X, r, cc); t_w = time.perf_counter() - t0
+    K = X.shape[1]
+    res["c3"] = {"sample": f"forward and dgrad on {rows} of 8192 rows, wgrad on {pts} of 4096^2 outputs",
+                 "fwd_TFLOPs": 2.0 * rows * W.shape[0] * K / t_f / 1e12,
+                 "dgrad_TFLOPs": 2.0 * rows * W.shape[0] * K / t_d / 1e12,
+                 "wgrad_TFLOPs": 2.0 * pts * X.shape[0] / t_w / 1e12,
+                 "seconds": round(t_f + t_d + t_w, 2)}
+    res["cores"] = oracle.threads()
+    return res
+
+
 def calibration_c() -> float:
     with open(os.path.join(ROOT, "tests", "golden", "c4_calibration.json")) as f:
         return float(json.load(f)["c"])
@@ -286,6 +518,7 @@ class Model:
         self.dB = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)
         self.dC = torch.empty((BATCH, WIDTH), dtype=f16, device=dev)   # unfused variant only
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.loss_ws = torch.empty(mp.loss_mse_workspace(BATCH, WIDTH), dtype=torch.uint8, device=dev)
         self.scaler = mp.Scaler(w.scale, w.dynamic, w.growth_interval)
         self.plist = mp.ParamList(self.W, self.V, self.G, self.W16)
         self.hp = (w.lr, w.momentum, w.weight_decay)
@@ -332,7 +565,8 @@ class Model:
                 t("fwd", mp.linear_fwd, inp, self.W16[l], Y=self.Z[l])
                 t("gelu_fwd", mp.act_fwd, mp.GELU, self.Z[l], self.H[l])
                 inp = self.H[l]
-        t("loss", mp.loss_mse, self.Z[-1], self.T, self.c, self.scaler, self.loss, self.dA)
+        t("loss", mp.loss_mse, self.Z[-1], self.T, self.c, self.scaler, self.loss, self.dA,
+          workspace=self.loss_ws)
         dZ, other = self.dA, self.dB
         for l in range(LAYERS - 1, -1, -1):
             prev = self.X if l == 0 else self.H[l - 1]
@@ -512,6 +746,24 @@ def main():
     fp32_reductions = reductions(model, mp, torch)
     c1 = c1_latency(mp, torch, workloads)
 
+    # The achievable denominators (stream probe, clock and MFMA rate under load), then the other
+    # configurations at full size: C3's single layer and the C2 / C5 update-only sweeps.
+    from mixed_precision_neural_amd import probe
+    ceiling = hbm_ceiling(torch, probe)
+    clock = mfma_clock(torch, probe)
+    copy_gbps = ceiling["copy"]["GBps"]
+    c3 = c3_gemms(mp, torch)
+    c2 = c2_sweep(mp, torch, copy_gbps)
+    c5 = c5_sweep(mp, torch, workloads, copy_gbps)
+    if args.no_cpu_baseline:
+        for d in (c2, c3, c5):
+            d.pop("_host")
+    else:
+        cpu = cpu_configs(c2, c3, c5)
+        for k, d in (("c2", c2), ("c3", c3), ("c5", c5)):
+            d["cpu_oracle"] = dict(cpu[k], cores=cpu["cores"])
+    torch.cuda.synchronize()
+
     gemm_flop = 2.0 * WIDTH * WIDTH * BATCH
     step_flop = gemm_flop * (3 * LAYERS - 1)
     value = step_flop / (ms * 1e-3) / 1e12
@@ -559,11 +811,17 @@ def main():
                     "traffic": measured_traffic("update", "update"),
                     "two_pass_us": round(two_pass_ms * 1e3, 2),
                     "two_pass_GBps": round(SWEEP_BYTES_PER_PARAM * nparam / (two_pass_ms * 1e-3) / 1e9, 1),
-                    "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam},
+                    "check_pass_bytes": CHECK_BYTES_PER_PARAM * nparam,
+                    "frac_of_copy_ceiling": round(sweep_gbps / copy_gbps, 4)},
         "mp_step_opt": variants,
         "absmax_method2": method2,
         "fp32_reductions": fp32_reductions,
         "c1_step_latency": c1,
+        "c2": c2,
+        "c3": c3,
+        "c5": c5,
+        "hbm_ceiling": ceiling,
+        "clock": clock,
         "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")
                    if k in kern},
         "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},

@@ -237,7 +237,11 @@ enum {
     MP_STEP_DEFAULT = 0,
     /* Skip the check pass: the gradients were produced by mp_linear_wgrad
      * with found_inf = &scaler->found_inf, which already holds the flag. */
-    MP_GRADS_PRECHECKED = 1u << 0
+    MP_GRADS_PRECHECKED = 1u << 0,
+    /* Only the check pass (Step 6): OR the overflow flag into scaler->found_inf
+     * and write nothing else (no unscale, no update). With
+     * MP_GRADS_PRECHECKED as well the call does nothing. */
+    MP_CHECK_ONLY = 1u << 1
 };
 
 /* One optimizer step. For every element of every tensor, in FP32 with one
@@ -400,22 +404,41 @@ mp_status mp_act_fwd(mp_act kind, const uint16_t* x, uint16_t* y, int64_t n, mp_
 mp_status mp_act_bwd(mp_act kind, const uint16_t* x, const uint16_t* dy, uint16_t* dx,
                      int64_t n, mp_stream stream);
 
+/* Bytes of device workspace mp_loss_softmax_ce needs for B rows of C logits
+ * (at most 4096; 0 when there is nothing to do). */
+size_t mp_loss_softmax_ce_workspace(int64_t B, int64_t C);
+
 /* Mean softmax cross-entropy over B rows of C logits (binary16, row-major,
  * contiguous) with int32 labels in [0, C). Writes the FP32 loss to *loss
  * (device) and dlogits = RNE16(S * (softmax - onehot) / B) with S read from
  * `scaler`. Labels live on the device, so their range is the caller's
- * responsibility: a label outside [0, C) contributes no one-hot term. */
+ * responsibility: a label outside [0, C) contributes no one-hot term.
+ * The loss is reduced in a fixed order: per-block partials in `workspace`
+ * (caller-owned device memory of at least mp_loss_softmax_ce_workspace(B, C)
+ * bytes, 4-byte aligned, overwritten), then one block. Calls with disjoint
+ * buffers and workspaces may run concurrently.
+ * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, a null pointer, too small
+ * or misaligned a workspace when B * C > 0), MP_ERR_HIP. */
 mp_status mp_loss_softmax_ce(const uint16_t* logits, const int32_t* labels, int64_t B,
                              int64_t C, const mp_scaler* scaler, float* loss,
-                             uint16_t* dlogits, mp_stream stream);
+                             uint16_t* dlogits, void* workspace, size_t workspace_bytes,
+                             mp_stream stream);
+
+/* Bytes of device workspace mp_loss_mse needs for M x N elements (at most
+ * 4096; 0 when there is nothing to do). */
+size_t mp_loss_mse_workspace(int64_t M, int64_t N);
 
 /* Mean squared error times c over the M x N elements (binary16, contiguous):
  * *loss = c * mean((y - t)^2) (FP32, device), dy = RNE16(S * c * 2 (y - t) / (M N)).
- * The sum is reduced in a fixed order (per-block partials in a library-owned
- * device array, then one block), so the loss is deterministic; concurrent
- * loss calls on one GPU share that array and must not overlap. */
+ * The sum is reduced in a fixed order: per-block partials in `workspace`
+ * (caller-owned device memory of at least mp_loss_mse_workspace(M, N) bytes,
+ * 4-byte aligned, overwritten), then one block; the loss is deterministic.
+ * Calls with disjoint buffers and workspaces may run concurrently.
+ * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, a null pointer, too small
+ * or misaligned a workspace when M * N > 0), MP_ERR_HIP. */
 mp_status mp_loss_mse(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N, float c,
-                      const mp_scaler* scaler, float* loss, uint16_t* dy, mp_stream stream);
+                      const mp_scaler* scaler, float* loss, uint16_t* dy, void* workspace,
+                      size_t workspace_bytes, mp_stream stream);
 
 /* ------------------------------------------------------------------------ */
 const char* mp_status_string(mp_status status);

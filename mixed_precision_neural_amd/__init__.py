@@ -23,8 +23,9 @@ __all__ = [
     "linear_fwd_act_deriv", "linear_dgrad_mul",
     "Scaler", "ParamList", "step", "step_opt", "TensorList", "absmax", "scaler_init_from_absmax",
     "round_f32_to_f16", "act_fwd", "act_bwd", "loss_softmax_ce", "loss_mse",
+    "loss_softmax_ce_workspace", "loss_mse_workspace",
     "bn_stats", "bn_apply", "softmax",
-    "MP_GRADS_PRECHECKED", "RELU", "GELU", "SGD", "NESTEROV", "ADAGRAD",
+    "MP_GRADS_PRECHECKED", "MP_CHECK_ONLY", "RELU", "GELU", "SGD", "NESTEROV", "ADAGRAD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mp.h")
 
 MP_F16, MP_F32 = 0, 1
 MP_GRADS_PRECHECKED = 1
+MP_CHECK_ONLY = 2
 RELU, GELU = 0, 1
 SGD, NESTEROV, ADAGRAD = 0, 1, 2          # mp_opt_kind
 _STATUS = {0: "MP_OK", 1: "MP_ERR_INVALID_ARGUMENT", 2: "MP_ERR_MISALIGNED",
@@ -93,8 +95,12 @@ def lib() -> C.CDLL:
         L.mp_round_f32_to_f16.argtypes = [vp, vp, i64, vp]
         L.mp_act_fwd.argtypes = [C.c_int, vp, vp, i64, vp]
         L.mp_act_bwd.argtypes = [C.c_int, vp, vp, vp, i64, vp]
-        L.mp_loss_softmax_ce.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
-        L.mp_loss_mse.argtypes = [vp, vp, i64, i64, C.c_float, vp, vp, vp, vp]
+        L.mp_loss_softmax_ce_workspace.argtypes = [i64, i64]
+        L.mp_loss_softmax_ce_workspace.restype = C.c_size_t
+        L.mp_loss_softmax_ce.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, C.c_size_t, vp]
+        L.mp_loss_mse_workspace.argtypes = [i64, i64]
+        L.mp_loss_mse_workspace.restype = C.c_size_t
+        L.mp_loss_mse.argtypes = [vp, vp, i64, i64, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.mp_bn_stats_workspace.argtypes = [i64, i64]
         L.mp_bn_stats_workspace.restype = C.c_size_t
         L.mp_bn_stats.argtypes = [vp, i64, i64, i64, vp, vp, vp, C.c_size_t, vp]
@@ -502,29 +508,56 @@ def softmax(x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torc
     return y
 
 
+def _workspace(ws, nbytes: int, align: int, device) -> torch.Tensor:
+    """ws (a GPU tensor of at least nbytes), or a new uint8 buffer of that size."""
+    if ws is None:
+        return torch.empty(max(nbytes, align), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous GPU tensor")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {nbytes} needed")
+    return ws
+
+
+def loss_softmax_ce_workspace(B: int, Cn: int) -> int:
+    """Bytes of workspace mp_loss_softmax_ce needs (a reusable buffer for ``workspace=``)."""
+    return int(lib().mp_loss_softmax_ce_workspace(B, Cn))
+
+
+def loss_mse_workspace(M: int, N: int) -> int:
+    """Bytes of workspace mp_loss_mse needs (a reusable buffer for ``workspace=``)."""
+    return int(lib().mp_loss_mse_workspace(M, N))
+
+
 def loss_softmax_ce(logits: torch.Tensor, labels: torch.Tensor, scaler: Scaler,
                     loss: torch.Tensor | None = None, dlogits: torch.Tensor | None = None,
-                    stream=None):
+                    stream=None, workspace: torch.Tensor | None = None):
     B, Cn = logits.shape
     _flat2(logits)
     if labels.dtype != torch.int32 or not labels.is_cuda or labels.numel() != B:
         raise TypeError("labels must be a GPU int32 tensor of length B")
     loss = _out(loss, (1,), torch.float32, logits.device)
     dlogits = _out(dlogits, (B, Cn), logits.dtype, logits.device)
+    nbytes = loss_softmax_ce_workspace(B, Cn)
+    ws = _workspace(workspace, nbytes, 4, logits.device)
     _check(lib().mp_loss_softmax_ce(C.c_void_p(logits.data_ptr()), C.c_void_p(labels.data_ptr()),
                                     B, Cn, scaler.ptr, C.c_void_p(loss.data_ptr()),
-                                    C.c_void_p(dlogits.data_ptr()), _stream(stream)),
+                                    C.c_void_p(dlogits.data_ptr()), C.c_void_p(ws.data_ptr()),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
            "mp_loss_softmax_ce")
     return loss, dlogits
 
 
 def loss_mse(y: torch.Tensor, t: torch.Tensor, c: float, scaler: Scaler,
-             loss: torch.Tensor | None = None, dy: torch.Tensor | None = None, stream=None):
+             loss: torch.Tensor | None = None, dy: torch.Tensor | None = None, stream=None,
+             workspace: torch.Tensor | None = None):
     M, N = y.shape
     _flat2(y, t)
     loss = _out(loss, (1,), torch.float32, y.device)
     dy = _out(dy, (M, N), y.dtype, y.device)
+    ws = _workspace(workspace, loss_mse_workspace(M, N), 4, y.device)
     _check(lib().mp_loss_mse(C.c_void_p(y.data_ptr()), C.c_void_p(t.data_ptr()), M, N, float(c),
                              scaler.ptr, C.c_void_p(loss.data_ptr()), C.c_void_p(dy.data_ptr()),
+                             C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                              _stream(stream)), "mp_loss_mse")
     return loss, dy

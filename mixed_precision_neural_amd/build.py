@@ -1,4 +1,5 @@
-"""Builds libmp.so (the HIP kernels and the C-ABI) in-tree for gfx950 with hipcc.
+"""Builds libmp.so (the HIP kernels and the C-ABI) in-tree for gfx950 with hipcc, and
+libmp_probe.so (the measurement probes of include/mp_probe.h, linked against libmp.so).
 
 Every translation unit is compiled with
   -ffp-contract=off   no fused multiply-add anywhere (the update is bit-exact
@@ -19,7 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmp.so")
+PROBE_LIB = os.path.join(HERE, "libmp_probe.so")
 SOURCES = ["mp_common.hip", "mp_step.hip", "mp_gemm.hip", "mp_aux.hip", "mp_stats.hip", "mp_reduce.hip"]
+PROBE_SOURCES = ["mp_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,20 +44,27 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compiles every source and links libmp.so next to this file. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+def _link(path: str, objs: list[str], libs: list[str]) -> None:
+    tmp = path + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *libs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compiles every source, links libmp.so and libmp_probe.so next to this file. Returns the
+    path of libmp.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra), srcs)))
+    _link(LIB, [objs[s] for s in SOURCES], [])
+    _link(PROBE_LIB, [objs[s] for s in PROBE_SOURCES], [f"-L{HERE}", "-lmp", "-Wl,-rpath,$ORIGIN"])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

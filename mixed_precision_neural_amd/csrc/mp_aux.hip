@@ -9,17 +9,18 @@
 //
 // Point-wise kernels read binary16, compute in FP32 and write binary16, with
 // 16-byte vectors when the buffers allow. The losses reduce in FP32 in a
-// fixed order (per-block partials in a library-owned device array, then a
-// single block), so the loss value is deterministic; the loss gradient is
-// S * dL/dy in FP32, rounded once to binary16. S is read from the device
-// scaler, so no host round trip is needed.
+// fixed order (per-block partials in a caller-owned workspace, then a single
+// block), so the loss value is deterministic and calls with disjoint buffers
+// share no device state; the loss gradient is S * dL/dy in FP32, rounded once
+// to binary16. S is read from the device scaler, so no host round trip is
+// needed.
 #include "mp_act.h"
+#include "mp_loss.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxPartials = 1024;
-__device__ float g_partials[kMaxPartials];
+constexpr int kMaxPartials = 1024;    // blocks of a loss kernel = FP32 partials in the workspace
 
 using mp::act_bwd1;
 using mp::act_fwd1;
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(kThreads) void softmax_ce_kernel(const uint16_t* __
                                                               const int32_t* __restrict__ labels,
                                                               int64_t B, int64_t C,
                                                               const mp_scaler* __restrict__ sc,
-                                                              uint16_t* __restrict__ dz) {
+                                                              uint16_t* __restrict__ dz,
+                                                              float* __restrict__ partials) {
     const float S = sc->scale;
     const float invB = 1.0f / float(B);
     const int lane = threadIdx.x & 63;
@@ -154,13 +156,14 @@ __global__ __launch_bounds__(kThreads) void softmax_ce_kernel(const uint16_t* __
         }
     }
     const float t = block_sum(part);
-    if (threadIdx.x == 0) g_partials[blockIdx.x] = t;
+    if (threadIdx.x == 0) partials[blockIdx.x] = t;
 }
 
 __global__ __launch_bounds__(kThreads) void mse_kernel(const uint16_t* __restrict__ y,
                                                        const uint16_t* __restrict__ t, int64_t n,
                                                        float coef, const mp_scaler* __restrict__ sc,
-                                                       uint16_t* __restrict__ dy, int vec) {
+                                                       uint16_t* __restrict__ dy, int vec,
+                                                       float* __restrict__ partials) {
     const float S = sc->scale;
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     const int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x;
@@ -192,14 +195,15 @@ __global__ __launch_bounds__(kThreads) void mse_kernel(const uint16_t* __restric
         dy[e] = mp::f2h(S * (coef * d));
     }
     const float s = block_sum(part);
-    if (threadIdx.x == 0) g_partials[blockIdx.x] = s;
+    if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
-// *loss = mul * sum(g_partials[0..count)), summed in index order by one thread
-// after a fixed-order per-thread pass.
-__global__ __launch_bounds__(kThreads) void finish_kernel(int count, float mul, float* loss) {
+// *loss = mul * sum(partials[0..count)): each thread adds its strided share in
+// index order, then the block sum (fixed order).
+__global__ __launch_bounds__(kThreads) void finish_kernel(const float* __restrict__ partials, int count,
+                                                          float mul, float* loss) {
     float v = 0.0f;
-    for (int i = threadIdx.x; i < count; i += kThreads) v += g_partials[i];
+    for (int i = threadIdx.x; i < count; i += kThreads) v += partials[i];
     const float t = block_sum(v);
     if (threadIdx.x == 0) *loss = t * mul;
 }
@@ -239,35 +243,74 @@ extern "C" mp_status mp_act_bwd(mp_act kind, const uint16_t* x, const uint16_t* 
     return mp::launch_status("mp_act_bwd");
 }
 
+namespace {
+uint32_t ce_grid(int64_t B) { return grid_for((B + 3) / 4 * kThreads); }
+uint32_t mse_grid(int64_t n) { return grid_for((n + 7) / 8); }
+bool ws_ok(const void* ws, size_t bytes, uint32_t grid) {
+    return ws && (reinterpret_cast<uintptr_t>(ws) & 3u) == 0 && bytes >= size_t(grid) * sizeof(float);
+}
+}  // namespace
+
+extern "C" size_t mp_loss_softmax_ce_workspace(int64_t B, int64_t C) {
+    if (B <= 0 || C <= 0) return 0;
+    return size_t(ce_grid(B)) * sizeof(float);
+}
+
+extern "C" size_t mp_loss_mse_workspace(int64_t M, int64_t N) {
+    if (M <= 0 || N <= 0) return 0;
+    return size_t(mse_grid(M * N)) * sizeof(float);
+}
+
 extern "C" mp_status mp_loss_softmax_ce(const uint16_t* logits, const int32_t* labels, int64_t B,
                                         int64_t C, const mp_scaler* scaler, float* loss,
-                                        uint16_t* dlogits, mp_stream stream) {
+                                        uint16_t* dlogits, void* workspace, size_t workspace_bytes,
+                                        mp_stream stream) {
     if (B < 0 || C < 0) return MP_ERR_INVALID_ARGUMENT;
     if (!scaler || !loss) return MP_ERR_INVALID_ARGUMENT;
     if (B > 0 && C > 0 && (!logits || !labels || !dlogits)) return MP_ERR_INVALID_ARGUMENT;
     if (B == 0 || C == 0) return MP_OK;
+    const uint32_t grid = ce_grid(B);
+    if (!ws_ok(workspace, workspace_bytes, grid)) return MP_ERR_INVALID_ARGUMENT;
+    float* partials = static_cast<float*>(workspace);
     hipStream_t s = mp::as_stream(stream);
-    const uint32_t grid = grid_for((B + 3) / 4 * kThreads);
-    softmax_ce_kernel<<<grid, kThreads, 0, s>>>(logits, labels, B, C, scaler, dlogits);
+    softmax_ce_kernel<<<grid, kThreads, 0, s>>>(logits, labels, B, C, scaler, dlogits, partials);
     if (mp_status st = mp::launch_status("mp_loss_softmax_ce")) return st;
-    finish_kernel<<<1, kThreads, 0, s>>>(int(grid), 1.0f / float(B), loss);
+    finish_kernel<<<1, kThreads, 0, s>>>(partials, int(grid), 1.0f / float(B), loss);
     return mp::launch_status("mp_loss_softmax_ce/finish");
 }
 
-extern "C" mp_status mp_loss_mse(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N,
-                                 float c, const mp_scaler* scaler, float* loss, uint16_t* dy,
-                                 mp_stream stream) {
-    if (M < 0 || N < 0 || !scaler || !loss) return MP_ERR_INVALID_ARGUMENT;
+namespace mp {
+// The MSE loss with its partials in `partials` (at least loss_mse_partials(M, N) floats);
+// the arguments are checked by the caller (loss_mse_args).
+mp_status loss_mse_into(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N, float c,
+                        const mp_scaler* scaler, float* loss, uint16_t* dy, float* partials,
+                        hipStream_t s) {
     const int64_t n = M * N;
-    if (n > 0 && (!y || !t || !dy)) return MP_ERR_INVALID_ARGUMENT;
-    if (n == 0) return MP_OK;
-    hipStream_t s = mp::as_stream(stream);
     const double mn = double(M) * double(N);
     const float coef = float(2.0 * double(c) / mn);
     const int vec = mp::aligned16(y) && mp::aligned16(t) && mp::aligned16(dy);
-    const uint32_t grid = grid_for((n + 7) / 8);
-    mse_kernel<<<grid, kThreads, 0, s>>>(y, t, n, coef, scaler, dy, vec);
+    const uint32_t grid = mse_grid(n);
+    mse_kernel<<<grid, kThreads, 0, s>>>(y, t, n, coef, scaler, dy, vec, partials);
     if (mp_status st = mp::launch_status("mp_loss_mse")) return st;
-    finish_kernel<<<1, kThreads, 0, s>>>(int(grid), float(double(c) / mn), loss);
+    finish_kernel<<<1, kThreads, 0, s>>>(partials, int(grid), float(double(c) / mn), loss);
     return mp::launch_status("mp_loss_mse/finish");
+}
+
+mp_status loss_mse_args(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N,
+                        const mp_scaler* scaler, const float* loss, const uint16_t* dy) {
+    if (M < 0 || N < 0 || !scaler || !loss) return MP_ERR_INVALID_ARGUMENT;
+    if (M > 0 && N > 0 && (!y || !t || !dy)) return MP_ERR_INVALID_ARGUMENT;
+    return MP_OK;
+}
+size_t loss_mse_partials(int64_t M, int64_t N) { return M > 0 && N > 0 ? mse_grid(M * N) : 0; }
+}  // namespace mp
+
+extern "C" mp_status mp_loss_mse(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N,
+                                 float c, const mp_scaler* scaler, float* loss, uint16_t* dy,
+                                 void* workspace, size_t workspace_bytes, mp_stream stream) {
+    if (mp_status st = mp::loss_mse_args(y, t, M, N, scaler, loss, dy)) return st;
+    if (M == 0 || N == 0) return MP_OK;
+    if (!ws_ok(workspace, workspace_bytes, mse_grid(M * N))) return MP_ERR_INVALID_ARGUMENT;
+    return mp::loss_mse_into(y, t, M, N, c, scaler, loss, dy, static_cast<float*>(workspace),
+                             mp::as_stream(stream));
 }

@@ -343,7 +343,7 @@ namespace {
 
 mp_status run_step(const mp_param_list* L, int kind, const Hyper& hp, mp_scaler* scaler,
                    uint32_t flags, mp_stream stream) {
-    if (flags & ~uint32_t(MP_GRADS_PRECHECKED)) return MP_ERR_UNSUPPORTED;
+    if (flags & ~uint32_t(MP_GRADS_PRECHECKED | MP_CHECK_ONLY)) return MP_ERR_UNSUPPORTED;
     if (L->chunks == 0) return MP_OK;
     hipStream_t s = mp::as_stream(stream);
     const uint32_t chunks = uint32_t(L->chunks);
@@ -351,6 +351,7 @@ mp_status run_step(const mp_param_list* L, int kind, const Hyper& hp, mp_scaler*
         check_kernel<<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, &scaler->found_inf);
         if (mp_status st = mp::launch_status("mp_step/check")) return st;
     }
+    if (flags & MP_CHECK_ONLY) return MP_OK;
     switch (kind) {
         case MP_OPT_SGD:
             update_kernel<MP_OPT_SGD><<<chunks, kThreads, 0, s>>>(L->d_desc, L->d_chunk_tensor, scaler, hp, chunks);

@@ -107,3 +107,44 @@ def test_product_package_does_not_touch_the_oracle():
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.h" not in text and "liboracle" not in text, f
+
+
+def test_loss_workspace_sizes_and_validation():
+    """The losses reduce through a caller workspace: its size is one FP32 partial per block (at
+    most 1024 blocks), and a missing, short or misaligned workspace is rejected before launch."""
+    L = mp.lib()
+    assert L.mp_loss_mse_workspace(0, 5) == 0 and L.mp_loss_softmax_ce_workspace(3, 0) == 0
+    assert L.mp_loss_mse_workspace(1, 8) == 4                       # one block
+    assert L.mp_loss_mse_workspace(4096, 4096) == 4096               # capped at 1024 blocks
+    assert L.mp_loss_softmax_ce_workspace(64, 10) == 64              # 4 rows per block
+    assert L.mp_loss_softmax_ce_workspace(10 ** 6, 10) == 4096
+    need = L.mp_loss_mse_workspace(8, 8)
+    assert L.mp_loss_mse(P, P, 8, 8, C.c_float(1.0), P, P, P, None, need, None) == INVALID
+    assert L.mp_loss_mse(P, P, 8, 8, C.c_float(1.0), P, P, P, P, need - 1, None) == INVALID
+    assert L.mp_loss_mse(P, P, 8, 8, C.c_float(1.0), P, P, P, C.c_void_p(0x1002), need, None) == INVALID
+    assert L.mp_loss_mse(None, None, 0, 8, C.c_float(1.0), P, P, None, None, 0, None) == 0
+    need = L.mp_loss_softmax_ce_workspace(8, 10)
+    assert L.mp_loss_softmax_ce(P, P, 8, 10, P, P, P, None, need, None) == INVALID
+    assert L.mp_loss_softmax_ce(P, P, 8, 10, P, P, P, P, need - 4, None) == INVALID
+    assert L.mp_loss_softmax_ce(P, P, -1, 10, P, P, P, P, need, None) == INVALID
+
+
+def test_probe_library_exports_and_validation():
+    """libmp_probe.so (the measurement probes of include/mp_probe.h) exports every function its
+    header declares and rejects bad arguments on the host."""
+    import re
+
+    from mixed_precision_neural_amd import probe
+    names = set(re.findall(r"^\s*mp_status\s+(mp_\w+)\s*\(", open(probe.HEADER_PATH).read(), re.M))
+    assert names == {"mp_probe_hbm", "mp_probe_mfma_clock"}
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert names <= exported
+    L = probe.lib()
+    assert L.mp_probe_hbm(7, P, P, 4096, 0, 0, None) == INVALID          # unknown mode
+    assert L.mp_probe_hbm(0, P, P, 4000, 0, 0, None) == INVALID          # not a multiple of 4096
+    assert L.mp_probe_hbm(0, None, P, 4096, 0, 0, None) == INVALID       # read needs a source
+    assert L.mp_probe_hbm(2, P, C.c_void_p(0x1008), 4096, 0, 0, None) == INVALID   # misaligned
+    khz = C.c_int32()
+    assert L.mp_probe_mfma_clock(0, 10, P, C.byref(khz), None) == INVALID
+    assert L.mp_probe_mfma_clock(1, 10, None, C.byref(khz), None) == INVALID

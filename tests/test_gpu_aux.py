@@ -14,7 +14,7 @@ import torch
 
 import mixed_precision_neural_amd as mp
 import oracle
-from gpu_util import dev_f16, f16_values, host_bits16, require_gpu
+from gpu_util import dev_f16, f16_values, host_bits16, host_f32, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -79,3 +79,42 @@ def test_mse(M, N, c, S):
     ref_loss, ref_d = oracle.mse(yb, tb, c, S)
     assert math.isclose(float(loss.item()), ref_loss, rel_tol=1e-5)
     assert within_ulp(host_bits16(d), ref_d, ulps=2)
+
+
+def test_losses_on_two_streams_share_no_state():
+    """Two streams run the same loss over and over on disjoint buffers and workspaces while
+    neither waits for the other: every loss value and gradient has the bits of a call run
+    alone. (A partials array shared between calls would mix the streams' sums.)"""
+    require_gpu()
+    reps, M, N = 24, 1024, 1536
+    rng = np.random.Generator(np.random.PCG64(11))
+    ys = [dev_f16(rng.standard_normal((M, N)).astype(np.float16).view(np.uint16)) for _ in range(2)]
+    ts = [dev_f16(rng.standard_normal((M, N)).astype(np.float16).view(np.uint16)) for _ in range(2)]
+    z = [dev_f16((rng.standard_normal((4096, 10)) * 4).astype(np.float16).view(np.uint16)) for _ in range(2)]
+    lab = [torch.from_numpy(rng.integers(0, 10, 4096).astype(np.int32)).cuda() for _ in range(2)]
+    sc = [mp.Scaler(2.0 ** 12, True), mp.Scaler(2.0 ** 3, True)]
+    alone = []
+    for s in range(2):
+        l1, d1 = mp.loss_mse(ys[s], ts[s], 3.0, sc[s])
+        l2, d2 = mp.loss_softmax_ce(z[s], lab[s], sc[s])
+        torch.cuda.synchronize()
+        alone.append((host_f32(l1).view(np.uint32), host_bits16(d1), host_f32(l2).view(np.uint32), host_bits16(d2)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    loss = [torch.zeros(reps, 2, device="cuda") for _ in range(2)]
+    dys = [[torch.empty(M, N, dtype=torch.float16, device="cuda") for _ in range(reps)] for _ in range(2)]
+    dzs = [[torch.empty(4096, 10, dtype=torch.float16, device="cuda") for _ in range(reps)] for _ in range(2)]
+    ws = [torch.empty(mp.loss_mse_workspace(M, N), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    wc = [torch.empty(mp.loss_softmax_ce_workspace(4096, 10), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for s in range(2):
+            with torch.cuda.stream(streams[s]):
+                mp.loss_mse(ys[s], ts[s], 3.0, sc[s], loss[s][r, 0:1], dys[s][r], workspace=ws[s])
+                mp.loss_softmax_ce(z[s], lab[s], sc[s], loss[s][r, 1:2], dzs[s][r], workspace=wc[s])
+    torch.cuda.synchronize()
+    for s in range(2):
+        got = host_f32(loss[s]).view(np.uint32)
+        assert (got[:, 0] == alone[s][0][0]).all() and (got[:, 1] == alone[s][2][0]).all(), s
+        for r in range(reps):
+            assert np.array_equal(host_bits16(dys[s][r]), alone[s][1]), (s, r)
+            assert np.array_equal(host_bits16(dzs[s][r]), alone[s][3]), (s, r)

@@ -40,6 +40,7 @@ class C1State:
         self.Z2 = torch.empty((64, 10), dtype=torch.float16, device="cuda")
         self.dZ2 = torch.empty_like(self.Z2)
         self.loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(mp.loss_softmax_ce_workspace(64, 10), dtype=torch.uint8, device="cuda")
 
     def step(self):
         """Fused ReLU epilogues, the overflow flag from the weight-gradient epilogues, one
@@ -47,7 +48,7 @@ class C1State:
         c = self.cfg
         mp.linear_fwd_act(mp.RELU, self.X, self.W16[0], Z=self.Z1, H=self.H1)
         mp.linear_fwd(self.H1, self.W16[1], Y=self.Z2)
-        mp.loss_softmax_ce(self.Z2, self.y, self.S, self.loss, self.dZ2)
+        mp.loss_softmax_ce(self.Z2, self.y, self.S, self.loss, self.dZ2, workspace=self.ws)
         mp.linear_wgrad(self.dZ2, self.H1, dW=self.G[1], found_inf=self.S.found_inf_ptr)
         mp.linear_dgrad_act(mp.RELU, self.dZ2, self.W16[1], self.Z1, dZ=self.dZ1)
         mp.linear_wgrad(self.dZ1, self.X, dW=self.G[0], found_inf=self.S.found_inf_ptr)

@@ -218,6 +218,33 @@ def test_prechecked_flag_skips_the_check_pass():
     pl.close()
 
 
+@pytest.mark.parametrize("where", [None, "first", "last"])
+def test_check_only_sets_the_flag_and_writes_nothing(where):
+    """MP_CHECK_ONLY runs the check pass alone (Step 6): the flag equals the oracle's check over
+    the ragged list, and no master, momentum or binary16 byte changes either way."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(9))
+    sizes = [4096 * 3 + 5, 13, 70001]
+    ws = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    vs = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    gs = [(rng.standard_normal(n) * 100).astype(np.float16).view(np.uint16) for n in sizes]
+    if where:
+        gs[2][0 if where == "first" else sizes[2] - 1] = 0xFC00
+    r = Run(ws, vs, gs)
+    before = [host_f32(t).copy() for t in r.d_w + r.d_v] + [host_bits16(t).copy() for t in r.d_16]
+    dS = mp.Scaler(2.0 ** 10, True)
+    pl = r.plist()
+    mp.step(pl, dS, 0.01, 0.9, 1e-4, flags=mp.MP_CHECK_ONLY)
+    assert dS.read()["found_inf"] == oracle.check_overflow(r.h_g) == (1 if where else 0)
+    after = [host_f32(t) for t in r.d_w + r.d_v] + [host_bits16(t) for t in r.d_16]
+    for a, b in zip(after, before):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # with the flag already set, the check leaves it set; with PRECHECKED it does nothing
+    mp.step(pl, dS, 0.01, 0.9, 1e-4, flags=mp.MP_CHECK_ONLY | mp.MP_GRADS_PRECHECKED)
+    assert dS.read()["found_inf"] == (1 if where else 0)
+    pl.close()
+
+
 def test_determinism():
     """Pin P10: the same inputs give the same bits twice."""
     require_gpu()
