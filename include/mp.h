@@ -440,6 +440,21 @@ mp_status mp_loss_mse(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N
                       const mp_scaler* scaler, float* loss, uint16_t* dy, void* workspace,
                       size_t workspace_bytes, mp_stream stream);
 
+/* mp_loss_mse for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * same kernels, results and errors as mp_loss_mse, with the per-block
+ * partials in a device array of the library (1024 floats per GPU, the most
+ * any size needs, kept until the process ends) instead of a workspace, so
+ * neither the call nor the library allocates anything. The array's address
+ * is looked up once per device on the first call there. Every call on one
+ * GPU shares that array: calls that overlap on one GPU (other streams, other
+ * host threads, replays of graphs that hold this call) race and must be
+ * ordered by the caller.
+ * Errors: as mp_loss_mse without the workspace ones; MP_ERR_UNSUPPORTED on a
+ * device index of 64 or more. */
+mp_status mp_loss_mse_noalloc(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N, float c,
+                              const mp_scaler* scaler, float* loss, uint16_t* dy, mp_stream stream);
+
 /* ------------------------------------------------------------------------ */
 const char* mp_status_string(mp_status status);
 /* The last HIP error seen by this library on the calling thread ("" if none). */

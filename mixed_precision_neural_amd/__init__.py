@@ -23,7 +23,7 @@ __all__ = [
     "linear_fwd_act_deriv", "linear_dgrad_mul",
     "Scaler", "ParamList", "step", "step_opt", "TensorList", "absmax", "scaler_init_from_absmax",
     "round_f32_to_f16", "act_fwd", "act_bwd", "loss_softmax_ce", "loss_mse",
-    "loss_softmax_ce_workspace", "loss_mse_workspace",
+    "loss_softmax_ce_workspace", "loss_mse_workspace", "loss_mse_noalloc",
     "bn_stats", "bn_apply", "softmax",
     "MP_GRADS_PRECHECKED", "MP_CHECK_ONLY", "RELU", "GELU", "SGD", "NESTEROV", "ADAGRAD",
 ]
@@ -101,6 +101,8 @@ def lib() -> C.CDLL:
         L.mp_loss_mse_workspace.argtypes = [i64, i64]
         L.mp_loss_mse_workspace.restype = C.c_size_t
         L.mp_loss_mse.argtypes = [vp, vp, i64, i64, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
+        L.mp_loss_mse_noalloc.argtypes = [vp, vp, i64, i64, C.c_float, vp, vp, vp, vp]
+        L.mp_loss_mse_noalloc.restype = C.c_int
         L.mp_bn_stats_workspace.argtypes = [i64, i64]
         L.mp_bn_stats_workspace.restype = C.c_size_t
         L.mp_bn_stats.argtypes = [vp, i64, i64, i64, vp, vp, vp, C.c_size_t, vp]
@@ -560,4 +562,18 @@ def loss_mse(y: torch.Tensor, t: torch.Tensor, c: float, scaler: Scaler,
                              scaler.ptr, C.c_void_p(loss.data_ptr()), C.c_void_p(dy.data_ptr()),
                              C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                              _stream(stream)), "mp_loss_mse")
+    return loss, dy
+
+
+def loss_mse_noalloc(y: torch.Tensor, t: torch.Tensor, c: float, scaler: Scaler, loss: torch.Tensor,
+                     dy: torch.Tensor, stream=None):
+    """mp_loss_mse_noalloc: loss_mse with the library's per-device scratch array instead of a
+    workspace. The outputs are the caller's; nothing is allocated by this call."""
+    M, N = y.shape
+    _flat2(y, t, dy)
+    if tuple(dy.shape) != (M, N) or loss.dtype != torch.float32 or loss.numel() < 1 or not loss.is_cuda:
+        raise ValueError("dy must be [M, N] and loss a float32 GPU tensor")
+    _check(lib().mp_loss_mse_noalloc(C.c_void_p(y.data_ptr()), C.c_void_p(t.data_ptr()), M, N, float(c),
+                                     scaler.ptr, C.c_void_p(loss.data_ptr()), C.c_void_p(dy.data_ptr()),
+                                     _stream(stream)), "mp_loss_mse_noalloc")
     return loss, dy

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmp.so")
 PROBE_LIB = os.path.join(HERE, "libmp_probe.so")
-SOURCES = ["mp_common.hip", "mp_step.hip", "mp_gemm.hip", "mp_aux.hip", "mp_stats.hip", "mp_reduce.hip"]
+SOURCES = ["mp_common.hip", "mp_step.hip", "mp_gemm.hip", "mp_aux.hip", "mp_stats.hip", "mp_reduce.hip",
+           "mp_noalloc.hip"]
 PROBE_SOURCES = ["mp_probe.hip"]
 ARCH = "gfx950"
 
