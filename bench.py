@@ -61,6 +61,13 @@ MEASURED_TRAFFIC = {
               "absmax": (394786.6, 7.5)},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+# Matrix-core occupancy and shader clock of the 4096^3 GEMM kernels from one rocprofv3 counter pass each
+# (SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES with the dispatch's start and end times, over
+# `bench.py --pmc-kernel <kind>`): busy = MFMA-busy cycles / (4 SIMDs x CU-busy cycles), clock = CU-busy
+# cycles per CU / kernel duration. Like MEASURED_TRAFFIC, reported while the GEMM sources are unchanged.
+MEASURED_MFMA = {"sha256": MEASURED_TRAFFIC["gemm"]["sha256"],
+                 "fwd": (0.843, 1324.0), "fwd_act_deriv": (0.737, 1382.0), "dgrad_mul": (0.810, 1335.0),
+                 "wgrad": (0.844, 1315.0)}
 # The large reductions at the pages' sizes: batch normalization over 32 images x 112 x 112
 # positions x 64 channels, and the softmax over the 793,471-word vocabulary (64 rows, row pitch
 # rounded up to 8 elements).
@@ -103,6 +110,14 @@ def measured_traffic(group: str, kind: str):
         return None
     fetch_kib, write_kib = t[kind]
     return round((fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024)
+
+
+def measured_mfma(kind: str):
+    """(MFMA-busy fraction, shader MHz) of a GEMM kind from the counter pass, or (None, None) once
+    the GEMM sources have changed."""
+    if source_sha256(MEASURED_TRAFFIC["gemm"]["src"]) != MEASURED_MFMA["sha256"] or kind not in MEASURED_MFMA:
+        return None, None
+    return MEASURED_MFMA[kind]
 
 
 def pmc_kernel(args, mp, torch):
@@ -492,6 +507,21 @@ def cpu_configs(c2, c3, c5) -> dict:
     return res
 
 
+def roofline_line(dom: str, g: dict) -> dict:
+    """The roofline object of the dominant GEMM kind: achieved TFLOP/s against the 2.5 PFLOP/s FP16
+    dense peak, the counter traffic, and, from the counter pass, how busy the matrix cores were and the
+    shader clock the chip ran this kernel at (the spec peak assumes 2.4 GHz)."""
+    busy, mhz = measured_mfma(dom)
+    out = {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": g["TFLOPs"], "peak": PEAK_F16_TFLOPS,
+           "unit": "TFLOP/s", "frac": g["frac"], "traffic": measured_traffic("gemm", dom),
+           "mfma_busy_frac": busy, "clock_mhz_under_load": mhz}
+    if mhz:
+        adj = PEAK_F16_TFLOPS * mhz / 2400.0
+        out["clock_adjusted_peak"] = round(adj, 1)
+        out["frac_of_clock_adjusted_peak"] = round(g["TFLOPs"] / adj, 4)
+    return out
+
+
 def calibration_c() -> float:
     with open(os.path.join(ROOT, "tests", "golden", "c4_calibration.json")) as f:
         return float(json.load(f)["c"])
@@ -799,9 +829,7 @@ def main():
                             "recompute": "in the GEMM epilogues, GELU'(Z) evaluated in the backward",
                             "separate": "separate point-wise kernels"}[model.gelu],
                    "loss_multiplier_c": c},
-        "roofline": {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": gemm[dom]["TFLOPs"],
-                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": gemm[dom]["frac"],
-                     "traffic": measured_traffic("gemm", dom)},
+        "roofline": roofline_line(dom, gemm[dom]),
         "gemm": gemm,
         "mp_step": {"bound": "hbm", "mode": "flag from the wgrad epilogues, one update pass",
                     "avg_us": round(sweep_ms * 1e3, 2),
