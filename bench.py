@@ -776,13 +776,13 @@ def main():
     fp32_reductions = reductions(model, mp, torch)
     c1 = c1_latency(mp, torch, workloads)
 
-    # The achievable denominators (stream probe, clock and MFMA rate under load), then the other
-    # configurations at full size: C3's single layer and the C2 / C5 update-only sweeps.
+    # C3's single layer, the achievable denominators (stream probe, clock and MFMA rate under a
+    # pure matrix-core load), then the C2 / C5 update-only sweeps.
     from mixed_precision_neural_amd import probe
+    c3 = c3_gemms(mp, torch)
     ceiling = hbm_ceiling(torch, probe)
     clock = mfma_clock(torch, probe)
     copy_gbps = ceiling["copy"]["GBps"]
-    c3 = c3_gemms(mp, torch)
     c2 = c2_sweep(mp, torch, copy_gbps)
     c5 = c5_sweep(mp, torch, workloads, copy_gbps)
     if args.no_cpu_baseline:
