@@ -308,19 +308,13 @@ struct DmaLoader {
             }
         }
     }
-    // region: the operand's part of the target stage; soff: the slab's byte offset in the panel.
-    // The loads carry the sc0 cache-policy bit: every byte of a slab is read once per CU, and
-    // with sc0 the forward and dgrad layouts ran ~3 % faster (4096^3 and 8192 x 4096 x 4096,
-    // interleaved timing, same bits); the wgrad layout was unchanged. The non-temporal bit made
-    // every layout 12-20 % slower.
-    static constexpr int kCachePolicy = 1;                   // sc0
+    // region: the operand's part of the target stage; soff: the slab's byte offset in the panel
     __device__ __forceinline__ void fetch(__attribute__((address_space(3))) uint8_t* region, uint32_t soff) const {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
         for (int t = 0; t < kPer; ++t)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(region + blk0 + t * 1024), 16, voff[t], soff, 0,
-                kCachePolicy);
+                rsrc, (__attribute__((address_space(3))) void*)(region + blk0 + t * 1024), 16, voff[t], soff, 0, 0);
 #endif
     }
 };
