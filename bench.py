@@ -457,6 +457,33 @@ def c3_gemms(mp, torch, reps=10, M=8192, N=4096, K=4096) -> dict:
     return out
 
 
+def cpu_c1_step(workloads, reps: int = 20) -> dict:
+    """The oracle's C1 training step (forward with ReLU, softmax-CE at S = 1024, wgrad and dgrad of
+    both layers, the sweep over 136,192 parameters), averaged over `reps` steps from the C1 inputs."""
+    import numpy as np
+
+    import oracle
+    cfg = workloads.c1()
+    W = [cfg.W1.reshape(-1).copy(), cfg.W2.reshape(-1).copy()]
+    V = [np.zeros_like(w) for w in W]
+    W16 = [oracle.f32_to_f16(w) for w in W]
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        w1, w2 = W16[0].reshape(512, 256), W16[1].reshape(10, 512)
+        z1 = oracle.linear_fwd(cfg.X16, w1, out_f16=True)
+        h1 = oracle.relu_fwd(z1)
+        z2 = oracle.linear_fwd(h1, w2, out_f16=True)
+        _, dz2 = oracle.softmax_ce(z2, cfg.labels, cfg.scale)
+        g2 = oracle.linear_wgrad(dz2, h1, out_f16=True)
+        dz1 = oracle.relu_bwd(z1, oracle.linear_dgrad(dz2, w2, out_f16=True))
+        g1 = oracle.linear_wgrad(dz1, cfg.X16, out_f16=True)
+        oracle.step(W, V, [g1.reshape(-1), g2.reshape(-1)], W16, cfg.lr, cfg.momentum, cfg.weight_decay,
+                    1.0 / cfg.scale)
+    dt = (time.perf_counter() - t0) / reps
+    return {"sample": f"the full C1 step, {reps} steps", "us_per_step": round(dt * 1e6, 1),
+            "cores": oracle.threads()}
+
+
 def cpu_configs(c2, c3, c5) -> dict:
     """The oracle on bounded samples of C2, C3 and C5 (CPU threads of the host)."""
     import numpy as np
@@ -792,6 +819,7 @@ def main():
         cpu = cpu_configs(c2, c3, c5)
         for k, d in (("c2", c2), ("c3", c3), ("c5", c5)):
             d["cpu_oracle"] = dict(cpu[k], cores=cpu["cores"])
+        c1["cpu_oracle"] = cpu_c1_step(workloads)
     torch.cuda.synchronize()
 
     gemm_flop = 2.0 * WIDTH * WIDTH * BATCH
