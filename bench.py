@@ -46,9 +46,9 @@ CHECK_BYTES_PER_PARAM = 2
 # source it was taken on: it is reported while the SHA-256 of those files still matches.
 MEASURED_TRAFFIC = {
     "gemm": {"src": ["mp_gemm.hip", "mp_internal.h", "mp_act.h"],
-             "sha256": "4633c02f4499c360e250eea66bcd017d0ba7494425c15234eb9a01ce44c83981",
-             "fwd": (98406.8, 32768.0), "fwd_act": (98476.2, 65536.0), "fwd_act_deriv": (98483.2, 65536.0),
-             "dgrad_act": (114874.2, 32768.0), "dgrad_mul": (114802.7, 32768.0), "wgrad": (98418.7, 32768.0)},
+             "sha256": "553bb939ea3c2156c2e081306f2c2621740ddd01925b4947376e47641a07ae49",
+             "fwd": (98406.8, 32768.0), "fwd_act": (98461.2, 65536.0), "fwd_act_deriv": (98476.2, 65536.0),
+             "dgrad_act": (114867.2, 32768.0), "dgrad_mul": (114802.8, 32768.0), "wgrad": (99192.4, 34304.0)},
     "update": {"src": ["mp_step.hip", "mp_internal.h"],
                "sha256": "e5ea3aff9795752032a623271d7738611019a843dd1fa5fd24887479ee853aeb",
                "update": (990844.1, 1972212.6), "nesterov": (990309.5, 1973116.0),
@@ -66,8 +66,8 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # `bench.py --pmc-kernel <kind>`): busy = MFMA-busy cycles / (4 SIMDs x CU-busy cycles), clock = CU-busy
 # cycles per CU / kernel duration. Like MEASURED_TRAFFIC, reported while the GEMM sources are unchanged.
 MEASURED_MFMA = {"sha256": MEASURED_TRAFFIC["gemm"]["sha256"],
-                 "fwd": (0.843, 1324.0), "fwd_act_deriv": (0.737, 1382.0), "dgrad_mul": (0.810, 1335.0),
-                 "wgrad": (0.844, 1315.0)}
+                 "fwd": (0.852, 1324.0), "fwd_act_deriv": (0.739, 1394.0), "dgrad_mul": (0.806, 1352.0),
+                 "wgrad": (0.855, 1316.0)}
 # The large reductions at the pages' sizes: batch normalization over 32 images x 112 x 112
 # positions x 64 channels, and the softmax over the 793,471-word vocabulary (64 rows, row pitch
 # rounded up to 8 elements).
@@ -318,26 +318,27 @@ def hbm_ceiling(torch, probe, gib: int = 4) -> dict:
     return out
 
 
-def mfma_clock(torch, probe, blocks: int = 256, ms_target: float = 25.0) -> dict:
-    """The shader clock under a binary16 matrix-core load (one block of four waves per CU, eight
-    independent v_mfma_f32_32x32x16_f16 chains per wave) and the MFMA rate it reaches."""
+def mfma_clock(torch, probe, operands: int, blocks: int = 256, ms_target: float = 25.0) -> dict:
+    """The shader clock and the MFMA rate under a pure binary16 matrix-core load (one block of four
+    waves per CU, eight independent v_mfma_f32_32x32x16_f16 chains per wave, sixteen MFMAs a round),
+    with near-constant operands (probe.CONSTANT) or random ones like a GEMM's (probe.RANDOM)."""
     out_t = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda")
-    iters = 2000
-    probe.mfma_clock(blocks, iters, out_t)                 # warm-up and sizing
-    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t), 1)
-    iters = max(2000, int(iters * ms_target / max(ms, 1e-3)))
-    khz = probe.mfma_clock(blocks, iters, out_t)
-    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t), 1)
+    iters = 1000
+    probe.mfma_clock(blocks, iters, out_t, operands)       # warm-up and sizing
+    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t, operands), 1)
+    iters = max(1000, int(iters * ms_target / max(ms, 1e-3)))
+    khz = probe.mfma_clock(blocks, iters, out_t, operands)
+    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t, operands), 1)
     t = out_t.cpu().numpy().reshape(blocks, 4).astype("float64")
     mhz = (t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2]) * khz / 1000.0
-    flop = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    flop = blocks * 4 * iters * 16 * 2.0 * 32 * 32 * 16
     tf = flop / (ms * 1e-3) / 1e12
     mhz_med = float(sorted(mhz)[len(mhz) // 2])
     return {"clock_mhz": round(mhz_med, 1), "clock_mhz_min": round(float(mhz.min()), 1),
             "mfma_f16_TFLOPs": round(tf, 1), "frac_of_spec": round(tf / PEAK_F16_TFLOPS, 4),
             "clock_adjusted_peak_TFLOPs": round(PEAK_F16_TFLOPS * mhz_med / 2400.0, 1),
             "kernel_ms": round(ms, 3), "realtime_khz": khz,
-            "load": f"{blocks} blocks x 4 waves, 8 independent MFMA chains per wave, {iters} rounds"}
+            "load": f"{blocks} blocks x 4 waves, 8 independent MFMA chains per wave, {iters} rounds of 16"}
 
 
 def sweep_config(mp, torch, name, tensors, scale, hyper, inject, reps, copy_gbps) -> dict:
@@ -534,14 +535,18 @@ def cpu_configs(c2, c3, c5) -> dict:
     return res
 
 
-def roofline_line(dom: str, g: dict) -> dict:
+def roofline_line(dom: str, g: dict, random_operand_tflops: float) -> dict:
     """The roofline object of the dominant GEMM kind: achieved TFLOP/s against the 2.5 PFLOP/s FP16
-    dense peak, the counter traffic, and, from the counter pass, how busy the matrix cores were and the
-    shader clock the chip ran this kernel at (the spec peak assumes 2.4 GHz)."""
+    dense peak, the counter traffic, from the counter pass how busy the matrix cores were and the
+    shader clock the chip ran this kernel at (the spec peak assumes 2.4 GHz), and the fraction of the
+    MFMA rate the chip sustains on random binary16 operands with no memory traffic at all (the
+    matrix-core probe measured in this run)."""
     busy, mhz = measured_mfma(dom)
     out = {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": g["TFLOPs"], "peak": PEAK_F16_TFLOPS,
            "unit": "TFLOP/s", "frac": g["frac"], "traffic": measured_traffic("gemm", dom),
-           "mfma_busy_frac": busy, "clock_mhz_under_load": mhz}
+           "mfma_busy_frac": busy, "clock_mhz_under_load": mhz,
+           "random_operand_mfma_ceiling": random_operand_tflops,
+           "frac_of_random_operand_ceiling": round(g["TFLOPs"] / random_operand_tflops, 4)}
     if mhz:
         adj = PEAK_F16_TFLOPS * mhz / 2400.0
         out["clock_adjusted_peak"] = round(adj, 1)
@@ -803,12 +808,14 @@ def main():
     fp32_reductions = reductions(model, mp, torch)
     c1 = c1_latency(mp, torch, workloads)
 
-    # C3's single layer, the achievable denominators (stream probe, clock and MFMA rate under a
-    # pure matrix-core load), then the C2 / C5 update-only sweeps.
+    # C3's single layer, the achievable denominators (stream probe; clock and MFMA rate under a
+    # pure matrix-core load with constant and with random operands), then the C2 / C5 update-only
+    # sweeps.
     from mixed_precision_neural_amd import probe
     c3 = c3_gemms(mp, torch)
     ceiling = hbm_ceiling(torch, probe)
-    clock = mfma_clock(torch, probe)
+    clock = {"constant_operands": mfma_clock(torch, probe, probe.CONSTANT),
+             "random_operands": mfma_clock(torch, probe, probe.RANDOM)}
     copy_gbps = ceiling["copy"]["GBps"]
     c2 = c2_sweep(mp, torch, copy_gbps)
     c5 = c5_sweep(mp, torch, workloads, copy_gbps)
@@ -857,7 +864,7 @@ def main():
                             "recompute": "in the GEMM epilogues, GELU'(Z) evaluated in the backward",
                             "separate": "separate point-wise kernels"}[model.gelu],
                    "loss_multiplier_c": c},
-        "roofline": roofline_line(dom, gemm[dom]),
+        "roofline": roofline_line(dom, gemm[dom], clock["random_operands"]["mfma_f16_TFLOPs"]),
         "gemm": gemm,
         "mp_step": {"bound": "hbm", "mode": "flag from the wgrad epilogues, one update pass",
                     "avg_us": round(sweep_ms * 1e3, 2),
@@ -877,7 +884,7 @@ def main():
         "c3": c3,
         "c5": c5,
         "hbm_ceiling": ceiling,
-        "clock": clock,
+        "mfma_probe": clock,
         "aux_us": {k: round(kern[k]["avg_ms"] * 1e3, 2) for k in ("gelu_fwd", "gelu_bwd", "loss", "scaler")
                    if k in kern},
         "scaler_after": {"scale": st["scale"], "skipped_steps": st["skipped_steps"]},

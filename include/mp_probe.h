@@ -8,7 +8,8 @@
  * Arithmetic with FP32 Accumulation" and §6.1 "Speedup Claims"); the
  * probes give the achievable HBM stream rates (read only, write only, and
  * the 1:1 read/write mix of the optimizer sweep) and the shader clock and
- * binary16 MFMA rate under a matrix-core load, next to the datasheet peaks.
+ * binary16 MFMA rate under a matrix-core load (constant or random operands),
+ * next to the datasheet peaks.
  *
  * Same conventions as mp.h: device pointers unless stated, `stream` is a
  * hipStream_t passed as void*, every call is asynchronous on it, argument
@@ -44,18 +45,28 @@ typedef enum {
 mp_status mp_probe_hbm(int32_t mode, const void* src, void* dst, size_t bytes, int32_t blocks,
                        int32_t nontemporal, mp_stream stream);
 
+typedef enum {
+    MP_PROBE_OPERANDS_CONSTANT = 0,  /* every MFMA takes the same few small multiples of 2^-8   */
+    MP_PROBE_OPERANDS_RANDOM = 1     /* random binary16 (sign, mantissa; exponent 2^-3..2^0),
+                                        sixteen different registers per wave in rotation       */
+} mp_probe_operands;
+
 /* Runs `blocks` blocks of four waves; every wave issues `iters` rounds of
- * eight independent v_mfma_f32_32x32x16_f16 (binary16 inputs, FP32 sums),
- * i.e. 8 * 32768 FLOP per round. Wave 0 of each block records its shader
+ * sixteen v_mfma_f32_32x32x16_f16 (binary16 inputs, FP32 sums) on eight
+ * independent chains, i.e. 16 * 32768 FLOP per round, with operands of the
+ * kind `operands` names. The matrix cores' power draw, and so the clock the
+ * chip holds, depends on how many operand bits change between MFMAs: the
+ * CONSTANT load shows the clock ceiling, the RANDOM load the MFMA rate the
+ * chip sustains on data like a GEMM's. Wave 0 of each block records its shader
  * clock counter (s_memtime) and the constant-rate counter (s_memrealtime)
  * before and after the loop: out[4 b + 0..3] = {clock start, clock end, real
  * start, real end} (device uint64, 4 * blocks entries). *realtime_khz (host)
  * receives the constant counter's rate. The shader clock in MHz under this
  * load is (clock end - start) / (real end - start) * realtime_khz / 1000.
- * Errors: MP_ERR_INVALID_ARGUMENT (blocks < 1, iters < 1, null pointers),
- * MP_ERR_HIP. */
-mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, uint64_t* out, int32_t* realtime_khz,
-                              mp_stream stream);
+ * Errors: MP_ERR_INVALID_ARGUMENT (blocks < 1, iters < 1, unknown operand
+ * kind, null pointers), MP_ERR_HIP. */
+mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, int32_t operands, uint64_t* out,
+                              int32_t* realtime_khz, mp_stream stream);
 
 #ifdef __cplusplus
 }

@@ -382,7 +382,9 @@ struct FragAddr {
 // only where this code says so. The loop is unrolled over the two stages, so
 // every LDS address is one of a few per-lane registers plus an immediate. Each
 // slab issues the next slab's loads into the other stage under its first two
-// sub-steps, waits for them at its end, then a barrier.
+// sub-steps and waits for them after its third at the slab's one barrier; its
+// fourth sub-step's MFMAs follow the barrier and cover the next slab's first
+// fragment reads.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int FM, int FN>
 __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, uint4* st1, int64_t row0,
                                                  int64_t col0, int lane, int wm, int wn,
@@ -426,7 +428,7 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
         lb.fetch(s8[stage] + kAStage, uint32_t(kt) * b_step);
     };
     // in the order the MFMAs consume them (A row block 0 with every B block
-    // first), so the first MFMA after a barrier waits for two reads, not five
+    // first), so the first MFMA of a sub-step waits for two reads, not five
     auto read_frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
         af[0] = fa.read(s8[stage], 0, kk, 0);
 #pragma unroll
@@ -443,32 +445,35 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     half8 af[2][FM], bf[2][FN];
-    // Prologue: slab 0 in stage 0.
+    // Prologue: slab 0 in stage 0, and its first fragments.
     if (loader) fetch(0, 0);
     wait_loads();
     __syncthreads();
+    read_frags(0, 0, af[0], bf[0]);
 
     // One slab in stage S; a loading wave (LD) loads its share of the next slab
-    // (or, after the last, a copy of it) into the other stage.
+    // (or, after the last, a copy of it) into the other stage. Sub-steps 0-2
+    // read the following sub-step's fragments under their MFMAs; then the
+    // slab's one barrier, after which the next slab has landed in the other
+    // stage and every read of stage S is done (sub-step 3's fragments were read
+    // before it), so sub-step 3's MFMAs run with the next slab's first
+    // fragments read beneath them.
     auto slab = [&](int kt, auto s_tag, auto ld_tag) {
         constexpr int S = decltype(s_tag)::value;
         constexpr bool LD = decltype(ld_tag)::value;
         if constexpr (LD) fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
-        read_frags(S, 0, af[0], bf[0]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3) read_frags(S, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+        for (int kk = 0; kk < 3; ++kk) {
+            read_frags(S, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
             mfma(af[kk & 1], bf[kk & 1], 0, kMfma);
         }
-        // Instruction order (groups are filled in program order): the first
-        // fragments, then each MFMA followed by the next sub-step's fragment
-        // reads (sub-steps 0-2: one after each of the first MFMAs with 16 per
-        // sub-step, spread evenly with 8) and, in a loading wave, loads of the
-        // next slab spread over sub-steps 0 and 1 (after every MFMA when a
-        // wave loads more blocks than a sub-step has MFMAs, else after every
-        // other one).
-        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-        for (int kk = 0; kk < 4; ++kk)
+        // Instruction order (groups are filled in program order): each MFMA
+        // followed by the next sub-step's fragment reads (one after each of the
+        // first MFMAs with 16 per sub-step, spread evenly with 8) and, in a
+        // loading wave, loads of the next slab spread over sub-steps 0 and 1
+        // (after every MFMA when a wave loads more blocks than a sub-step has
+        // MFMAs, else after every other one).
+        for (int kk = 0; kk < 3; ++kk)
             for (int m = 0; m < kMfma; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (LD && kLoads <= kMfma && kk < 2 && !(m & 1) && kk * (kMfma / 2) + m / 2 < kLoads)
@@ -476,11 +481,22 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
                 if (LD && kLoads > kMfma && kk < 2 && kk * kMfma + m < kLoads)
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 const int nr = kMfma == 16 ? int(m < kReads) : (m + 1) * kReads / kMfma - m * kReads / kMfma;
-                if (kk < 3)
-                    for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+        // The barrier stays exactly here: without the fences the scheduler
+        // moves sub-step 3's MFMAs below it, where they no longer cover the next
+        // slab's first reads.
+        __builtin_amdgcn_sched_barrier(0);
         wait_loads();
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(S ^ 1, 0, af[0], bf[0]);
+        mfma(af[1], bf[1], 0, kMfma);
+        for (int m = 0; m < kMfma; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            const int nr = kMfma == 16 ? int(m < kReads) : (m + 1) * kReads / kMfma - m * kReads / kMfma;
+            for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -503,6 +519,9 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
             slab(kt + 1, C1(), NoLoad());
         }
     }
+    // The last slab read its (unused) successor's first fragments from the
+    // idle stage; the epilogue stages the output through both stages.
+    __syncthreads();
 }
 
 // Applies the binary16 point-wise tail of the epilogue to one output element

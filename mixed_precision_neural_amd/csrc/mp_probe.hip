@@ -1,5 +1,6 @@
-// Measurement probes (libmp_probe.so): achievable HBM stream rates and the
-// shader clock under a binary16 matrix-core load. They give the measured
+// Measurement probes (libmp_probe.so): achievable HBM stream rates, and the
+// shader clock and binary16 MFMA rate under a matrix-core load with constant
+// or random operands. They give the measured
 // denominators beside the datasheet peaks for the hot path's kernels, whose
 // bounds the source names: point-wise work and weight updates limited by
 // memory bandwidth or latency, dot products by arithmetic ("Mixed Precision
@@ -78,16 +79,42 @@ __global__ __launch_bounds__(kThreads) void hbm_kernel(const mp::u32x4* __restri
     }
 }
 
+// A 32-bit integer hash (two multiply-xorshift rounds) for the probe's operand data.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7FEB352Du;
+    x ^= x >> 15;
+    x *= 0x846CA68Bu;
+    x ^= x >> 16;
+    return x;
+}
+
 // Eight independent accumulator chains per wave keep the matrix core issuing
-// back to back with one wave per SIMD.
+// back to back with one wave per SIMD; a round is sixteen MFMAs, two on each
+// chain, taking operand pair (a[j], b[j + 3]) then (a[j + 5], b[j]) (indices
+// mod 8). CONSTANT: all eight A and B registers hold the same few small
+// multiples of 2^-8 (almost no bits change between MFMAs). RANDOM: each of the
+// sixteen registers holds its own random binary16 values (random sign and
+// 10-bit mantissa, exponent 2^-3 .. 2^0, like unit-scale activations and
+// weights), so consecutive MFMAs see unrelated operands, as in a GEMM.
+template <int OPERANDS>
 __global__ __launch_bounds__(kThreads) void mfma_clock_kernel(int iters, uint64_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
-    half8 a, b;
+    const uint32_t seed = probe_hash(uint32_t(blockIdx.x) * kThreads + threadIdx.x + 1u);
+    half8 a[8], b[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a[i] = _Float16(0.00390625f * float((lane + i) & 3));       // multiples of 2^-8, exact sums
-        b[i] = _Float16(0.00390625f * float((lane * 3 + i) & 3));
-    }
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (OPERANDS == MP_PROBE_OPERANDS_CONSTANT) {
+                a[p][i] = _Float16(0.00390625f * float((lane + i) & 3));
+                b[p][i] = _Float16(0.00390625f * float((lane * 3 + i) & 3));
+            } else {
+                const uint32_t ya = probe_hash(seed ^ uint32_t(16 * p + i)), yb = probe_hash(seed ^ uint32_t(16 * p + 8 + i));
+                a[p][i] = __builtin_bit_cast(_Float16, uint16_t((ya & 0x83FFu) | ((0xCu + ((ya >> 10) & 3u)) << 10)));
+                b[p][i] = __builtin_bit_cast(_Float16, uint16_t((yb & 0x83FFu) | ((0xCu + ((yb >> 10) & 3u)) << 10)));
+            }
+        }
     floatx16 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -97,7 +124,9 @@ __global__ __launch_bounds__(kThreads) void mfma_clock_kernel(int iters, uint64_
     const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[(j + 3) & 7], acc[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[(j + 5) & 7], b[j], acc[j], 0, 0, 0);
     }
     float s = 0.0f;
 #pragma unroll
@@ -111,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void mfma_clock_kernel(int iters, uint64_
         o[0] = c0;
         o[1] = c1;
         o[2] = r0;
-        // the sums are finite and non-negative; a negative one (never) would flag r1
-        o[3] = s < 0.0f ? 0 : r1;
+        // the sums are finite; testing them keeps the MFMAs live
+        o[3] = __builtin_isnan(s) ? 0 : r1;
     }
 }
 
@@ -144,14 +173,18 @@ extern "C" mp_status mp_probe_hbm(int32_t mode, const void* src, void* dst, size
     return mp::launch_status("mp_probe_hbm");
 }
 
-extern "C" mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, uint64_t* out, int32_t* realtime_khz,
-                                         mp_stream stream) {
+extern "C" mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, int32_t operands, uint64_t* out,
+                                         int32_t* realtime_khz, mp_stream stream) {
     if (blocks < 1 || iters < 1 || !out || !realtime_khz) return MP_ERR_INVALID_ARGUMENT;
+    if (operands != MP_PROBE_OPERANDS_CONSTANT && operands != MP_PROBE_OPERANDS_RANDOM) return MP_ERR_INVALID_ARGUMENT;
     int dev = 0, khz = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
     if (e != hipSuccess) return mp::hip_status(e, "mp_probe_mfma_clock");
     *realtime_khz = khz;
-    mfma_clock_kernel<<<uint32_t(blocks), kThreads, 0, mp::as_stream(stream)>>>(iters, out);
+    if (operands == MP_PROBE_OPERANDS_CONSTANT)
+        mfma_clock_kernel<MP_PROBE_OPERANDS_CONSTANT><<<uint32_t(blocks), kThreads, 0, mp::as_stream(stream)>>>(iters, out);
+    else
+        mfma_clock_kernel<MP_PROBE_OPERANDS_RANDOM><<<uint32_t(blocks), kThreads, 0, mp::as_stream(stream)>>>(iters, out);
     return mp::launch_status("mp_probe_mfma_clock");
 }

@@ -1,6 +1,7 @@
-"""Binding of libmp_probe.so (include/mp_probe.h): the achievable HBM stream rates and the shader
-clock under a binary16 matrix-core load, measured beside the datasheet peaks. Argument marshalling
-only; the probes run in their own HIP kernels. The import fails loudly when the library is missing.
+"""Binding of libmp_probe.so (include/mp_probe.h): the achievable HBM stream rates, and the shader
+clock and MFMA rate under a binary16 matrix-core load with constant or random operands, measured
+beside the datasheet peaks. Argument marshalling only; the probes run in their own HIP kernels.
+The import fails loudly when the library is missing.
 """
 from __future__ import annotations
 
@@ -15,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmp_probe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mp_probe.h")
 READ, WRITE, COPY = 0, 1, 2
+CONSTANT, RANDOM = 0, 1      # operand kinds of the matrix-core probe
 
 _lib = None
 
@@ -29,7 +31,7 @@ def lib() -> C.CDLL:
         vp, i32 = C.c_void_p, C.c_int32
         L.mp_probe_hbm.argtypes = [i32, vp, vp, C.c_size_t, i32, i32, vp]
         L.mp_probe_hbm.restype = C.c_int
-        L.mp_probe_mfma_clock.argtypes = [i32, i32, vp, C.POINTER(i32), vp]
+        L.mp_probe_mfma_clock.argtypes = [i32, i32, i32, vp, C.POINTER(i32), vp]
         L.mp_probe_mfma_clock.restype = C.c_int
         _lib = L
     return _lib
@@ -43,12 +45,12 @@ def hbm(mode: int, src: torch.Tensor | None, dst: torch.Tensor, nbytes: int, blo
                               _stream(stream)), "mp_probe_hbm")
 
 
-def mfma_clock(blocks: int, iters: int, out: torch.Tensor, stream=None) -> int:
-    """One launch of the matrix-core clock probe; out: int64 GPU tensor of 4 * blocks entries.
-    Returns the constant counter's rate in kHz."""
+def mfma_clock(blocks: int, iters: int, out: torch.Tensor, operands: int = CONSTANT, stream=None) -> int:
+    """One launch of the matrix-core probe (operands: CONSTANT or RANDOM); out: int64 GPU tensor of
+    4 * blocks entries. Returns the constant counter's rate in kHz."""
     if out.dtype != torch.int64 or out.numel() < 4 * blocks or not out.is_cuda:
         raise ValueError("out must be an int64 GPU tensor of 4 * blocks entries")
     khz = C.c_int32(0)
-    _check(lib().mp_probe_mfma_clock(int(blocks), int(iters), C.c_void_p(out.data_ptr()), C.byref(khz),
-                                     _stream(stream)), "mp_probe_mfma_clock")
+    _check(lib().mp_probe_mfma_clock(int(blocks), int(iters), int(operands), C.c_void_p(out.data_ptr()),
+                                     C.byref(khz), _stream(stream)), "mp_probe_mfma_clock")
     return int(khz.value)
