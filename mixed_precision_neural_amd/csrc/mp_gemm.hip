@@ -16,24 +16,26 @@
 //
 // Per block: a BM x BN output tile, BK = 64 reduction slices staged through
 // LDS in two buffers; the next slice's global loads are in flight while the
-// current slice feeds the MFMAs (v_mfma_f32_32x32x16_f16: binary16 inputs,
-// exact products, FP32 sums). Each operand keeps its global layout in LDS, so
-// every global load and LDS store is a plain 16-byte vector:
+// current slice feeds the MFMAs (v_mfma_f32_16x16x32_f16: binary16 inputs,
+// exact products, FP32 sums; on random data it draws less power per FLOP than
+// the 32 x 32 x 16 form, so the chip holds a higher clock under it). Each
+// operand keeps its global layout in LDS, so every global load and LDS store
+// is a plain 16-byte vector:
 //   KC tile: ROWS rows of 64 reduction elements (128 bytes, 8 chunks of 16
-//     bytes), chunk c of row r at r*8 + (c ^ ((r ^ r>>3) & 7)); an MFMA
-//     fragment row is one ds_read_b128.
+//     bytes), chunk c of row r at r*8 + (c ^ (r & 7)); an MFMA fragment row is
+//     one ds_read_b128, and the 16 rows x 4 chunks of a fragment read hit
+//     every LDS bank once.
 //   MN tile: 64 reduction rows of ROWS index elements, chunk c of row k at
-//     k*ROWS/8 + (c ^ (4*(k & 3) mod ROWS/8)); an MFMA fragment is two
-//     ds_read_b64_tr_b16, whose lane j of each 16-lane group collects element j
-//     of the four 8-byte pieces its group reads, i.e. four reduction values of
-//     one index column.
-// Both swizzles keep the fragment reads of the 256-wide tiles free of LDS bank
-// conflicts. Whole 256 x 256 tiles take a loop unrolled over the two LDS
-// stages: 8 waves of 128 x 64, two per SIMD, one of which loads the next slab
-// straight from global memory into LDS (buffer loads with scalar slab offsets)
-// while its partner only reads fragments and issues MFMAs; fragment addresses
-// are a few per-lane registers plus immediates, and an explicit instruction
-// order puts the loads and the next sub-step's LDS reads between the MFMAs.
+//     k*ROWS/8 + (c ^ swz_mn(k)); an MFMA fragment is two ds_read_b64_tr_b16,
+//     whose lane j of each 16-lane group collects element j of the four
+//     8-byte pieces its group reads, i.e. four reduction values of one index
+//     column.
+// Whole 256 x 256 tiles take a loop unrolled over the two LDS stages: 8 waves
+// of 128 x 64, two per SIMD, one of which loads the next slab straight from
+// global memory into LDS (buffer loads with scalar slab offsets) while its
+// partner only reads fragments and issues MFMAs; fragment addresses are a few
+// per-lane registers plus immediates, and an explicit instruction order puts
+// the loads and the next step's LDS reads between the MFMAs.
 // Edge tiles and small grids use a general loop with clamped, zero-filled
 // loads staged through registers.
 // Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
@@ -48,7 +50,7 @@
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -81,9 +83,9 @@ constexpr int kEpiDact = 3;      // C = act'(Z) * RNE16(acc), rounded once  (dgr
 constexpr int kEpiActD = 4;      // Z = RNE16(acc) (not stored): C = act(Z), C2 = RNE16(act'(Z))
 constexpr int kEpiMul = 5;       // C = RNE16(RNE16(acc) * D), D = Z the stored act'  (dgrad with act' saved)
 
-__device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_kc(int row) { return row & 7; }
 template <int CHUNKS>
-__device__ __forceinline__ int swz_mn(int krow) { return ((krow & 3) << 2) & (CHUNKS - 1); }
+__device__ __forceinline__ int swz_mn(int krow) { return ((krow & 3) << 2 ^ ((krow >> 3) & 1) << 1) & (CHUNKS - 1); }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
@@ -159,23 +161,23 @@ struct TileLoader {
     }
 };
 
-// MFMA fragment of index rows [r0, r0 + 32) for reduction sub-step kk (16
+// MFMA fragment of index rows [r0, r0 + 16) for reduction step ks (32
 // values) from one operand's LDS tile of ROWS index rows: lane l holds index
-// r0 + (l & 31) and the 8 reduction values 16*kk + 8*(l >> 5) .. + 7.
+// r0 + (l & 15) and the 8 reduction values 32 ks + 8 (l >> 4) .. + 7.
 template <int ROWS, bool KC>
-__device__ __forceinline__ half8 frag(const uint4* tile, int r0, int kk, int lane) {
+__device__ __forceinline__ half8 frag(const uint4* tile, int r0, int ks, int lane) {
     if (KC) {
-        const int row = r0 + (lane & 31);
-        const int c = 2 * kk + (lane >> 5);
+        const int row = r0 + (lane & 15);
+        const int c = 4 * ks + (lane >> 4);
         return __builtin_bit_cast(half8, tile[row * kRowChunks + (c ^ swz_kc(row))]);
     } else {
         constexpr int kMnChunks = ROWS / 8;
         const int g4 = lane >> 4, ii = lane & 15;
-        const int n = r0 + 16 * (g4 & 1) + 4 * (ii & 3);
+        const int n = r0 + 4 * (ii & 3);
         short4_t v[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int krow = 16 * kk + 8 * (g4 >> 1) + 4 * h + (ii >> 2);
+            const int krow = 32 * ks + 8 * g4 + 4 * h + (ii >> 2);
             const int chunk = krow * kMnChunks + ((n >> 3) ^ swz_mn<kMnChunks>(krow));
             const __attribute__((address_space(3))) uint8_t* p =
                 (const __attribute__((address_space(3))) uint8_t*)(tile + chunk) + ((n >> 2) & 1) * 8;
@@ -190,10 +192,9 @@ __device__ __forceinline__ half8 frag(const uint4* tile, int r0, int kk, int lan
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, bool FULL, int FM, int FN>
 __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* st0, uint4* st1, int64_t row0, int64_t col0,
                                             int tid, int lane, int wm, int wn,
-                                            floatx16 (&acc)[FM][FN]) {
+                                            floatx4 (&acc)[FM][FN]) {
     constexpr int NT = 64 * WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    constexpr int kStage = (BM + BN) * kRowChunks;   // uint4 per LDS stage
     TileLoader<BM, NT, A_KC> la;
     TileLoader<BN, NT, B_KC> lb;
     const int nk = int((g.R + kBK - 1) / kBK);
@@ -204,57 +205,27 @@ __device__ __forceinline__ void reduce_tile(const GemmArgs& g, uint4* st0, uint4
     lb.store(st0 + BM * kRowChunks, tid);
     __syncthreads();
 
-    auto read_frags = [&](const uint4* st, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
+    auto read_frags = [&](const uint4* st, int ks, half8 (&af)[FM], half8 (&bf)[FN]) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = frag<BM, A_KC>(st, wm * WTM + i * 32, kk, lane);
+        for (int i = 0; i < FM; ++i) af[i] = frag<BM, A_KC>(st, wm * WTM + i * 16, ks, lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[j] = frag<BN, B_KC>(st + BM * kRowChunks, wn * WTN + j * 32, kk, lane);
+        for (int j = 0; j < FN; ++j) bf[j] = frag<BN, B_KC>(st + BM * kRowChunks, wn * WTN + j * 16, ks, lane);
     };
-    // All four sub-steps of one slice, with the fragments of sub-step kk+1
-    // read while the MFMAs of sub-step kk run.
+    // The two reduction steps of one slice.
     auto slice = [&](const uint4* st) {
-        half8 af[2][FM], bf[2][FN];
-        read_frags(st, 0, af[0], bf[0]);
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int c = kk & 1;
-            if (kk + 1 < kBK / 16) read_frags(st, kk + 1, af[c ^ 1], bf[c ^ 1]);
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            half8 af[FM], bf[FN];
+            read_frags(st, ks, af, bf);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
         }
     };
 
     int kt = 0;
-    if (FULL && FM * FN == 16 && TileLoader<BM, NT, A_KC>::kPer + TileLoader<BN, NT, B_KC>::kPer == 16) {
-        // Steady state: every slice but the last, one basic block per slice.
-        constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per sub-step
-        static_assert(kReads <= 16, "at most one LDS read per MFMA");
-        for (; kt + 1 < nk; ++kt) {
-            const int cur = kt & 1;
-            const int64_t k0 = int64_t(kt + 1) * kBK;
-            la.template load<FULL>(g.A, g.lda, g.Mc, g.R, row0, k0, tid);
-            lb.template load<FULL>(g.B, g.ldb, g.Nc, g.R, col0, k0, tid);
-            slice(cur ? st1 : st0);
-            uint4* nxt = cur ? st0 : st1;
-            la.store(nxt, tid);
-            lb.store(nxt + BM * kRowChunks, tid);
-            // Instruction order of the slice (groups are filled in program order).
-            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);            // sub-step 0 fragments
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-                    if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // global load
-                    if (kk < 3 && m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                    if (kk == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);            // LDS store
-                }
-            __syncthreads();
-        }
-    }
     for (; kt < nk; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nk;
@@ -321,53 +292,48 @@ struct DmaLoader {
 
 // Per-lane LDS byte addresses of one operand's MFMA fragments, folded so that
 // everything but the lane-dependent XOR swizzle is an immediate offset of the
-// ds_read (the stage, the 32-row block pairs, the reduction sub-step):
-//   KC: fragment (i, kk) of a wave's rows R0 + 32 i + (lane & 31) sits at
-//       row * 128 + 16 * ((2 kk + lane / 32) ^ swz_kc(row)); for rows 32 apart
-//       the swizzle differs only in bit 2 (i odd), so 8 addresses (kk, i & 1)
-//       cover all 16, plus 4096 i.
-//   MN: fragment (j, kk) reads reduction rows 16 kk + ...; the chunk swizzle
-//       depends only on the lane, so 8 addresses (j, h) plus kk * 256 * ROWS/8
-//       cover all, h being the two transposing reads of a fragment.
+// ds_read (the stage, the 16-row blocks, the reduction step):
+//   KC: fragment (i, ks) of a wave's rows R0 + 16 i + (lane & 15) is chunk
+//       4 ks + lane / 16 of its row, stored at that chunk ^ (row & 7) =
+//       (lane / 16 ^ lane & 7) ^ 4 ks: two addresses (ks), plus 2048 i.
+//   MN: fragment (j, ks) of the wave's 16-column block j takes reduction rows
+//       32 ks + 8 (lane / 16) + 4 h + (lane & 15) / 4 (h: its two transposing
+//       reads). The chunk swizzle depends on the lane only (it leaves bits 2
+//       and 5 of the reduction row alone), so one address per block j covers
+//       both reads and both steps (h and ks immediates).
 typedef const __attribute__((address_space(3))) uint8_t lds_u8;
 
-template <int ROWS, bool KC>
+template <int ROWS, bool KC, int NBLK>
 struct FragAddr {
-    uint32_t a[8];
-    // r0w: first index row of the wave's block; base: byte offset of the operand's stage 0
+    static constexpr int kRegs = KC ? 2 : NBLK;
+    static constexpr int C = ROWS / 8;                       // 16-byte chunks per MN reduction row
+    uint32_t a[kRegs];
+    // r0w: first index row of the wave's block (a multiple of 16); base: byte offset of the operand's stage 0
     __device__ __forceinline__ void init(int r0w, int lane, uint32_t base) {
         if (KC) {
-            const int l = lane & 31, h = lane >> 5;
+            const int x = (lane >> 4) ^ (lane & 7);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int p = 0; p < 2; ++p)
-                    a[kk * 2 + p] = base + uint32_t((r0w + l) * 128 + 16 * ((2 * kk + h) ^ swz_kc(l) ^ (4 * p)));
+            for (int ks = 0; ks < 2; ++ks) a[ks] = base + uint32_t((r0w + (lane & 15)) * 128 + 16 * (x ^ (4 * ks)));
         } else {
-            constexpr int C = ROWS / 8;
             const int g4 = lane >> 4, ii = lane & 15;
-            const int sw = swz_mn<C>(ii >> 2);
+            const int k0 = 8 * g4 + (ii >> 2);
+            const int sw = swz_mn<C>(k0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = r0w + 32 * j + 16 * (g4 & 1) + 4 * (ii & 3);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    a[j * 2 + h] = base + uint32_t((8 * (g4 >> 1) + 4 * h + (ii >> 2)) * C * 16 +
-                                                   16 * ((n >> 3) ^ sw) + 8 * (ii & 1));
+            for (int j = 0; j < kRegs; ++j) {
+                const int n = r0w + 16 * j + 4 * (ii & 3);
+                a[j] = base + uint32_t(k0 * C * 16 + 16 * ((n >> 3) ^ sw) + 8 * (ii & 1));
             }
         }
     }
-    // fragment idx (i for KC rows, j for MN columns) of sub-step kk; off: stage offset in bytes
-    __device__ __forceinline__ half8 read(lds_u8* lds, int idx, int kk, uint32_t off) const {
+    // fragment idx (i for KC rows, j for MN columns) of reduction step ks; off: stage offset in bytes
+    __device__ __forceinline__ half8 read(lds_u8* lds, int idx, int ks, uint32_t off) const {
         if (KC) {
-            return *reinterpret_cast<const __attribute__((address_space(3))) half8*>(
-                lds + a[kk * 2 + (idx & 1)] + 4096 * idx + off);
+            return *reinterpret_cast<const __attribute__((address_space(3))) half8*>(lds + a[ks] + 2048 * idx + off);
         } else {
-            constexpr uint32_t kStep = 256 * (ROWS / 8);     // bytes per 16 reduction rows
-            short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4*)(lds + a[idx * 2 + 0] + kk * kStep + off));
-            short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4*)(lds + a[idx * 2 + 1] + kk * kStep + off));
+            constexpr uint32_t kStep = 32 * C * 16, kHalf = 4 * C * 16;   // bytes per 32 and per 4 reduction rows
+            const uint32_t o = a[idx] + ks * kStep + off;
+            short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(lds + o));
+            short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(lds + o + kHalf));
             const short8_t w = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             return __builtin_bit_cast(half8, w);
         }
@@ -380,32 +346,35 @@ struct FragAddr {
 // stages are separate variables so that the compiler can tell a fragment read
 // of one stage from a load in flight into the other and waits for those loads
 // only where this code says so. The loop is unrolled over the two stages, so
-// every LDS address is one of a few per-lane registers plus an immediate. Each
-// slab issues the next slab's loads into the other stage under its first two
-// sub-steps and waits for them after its third at the slab's one barrier; its
-// fourth sub-step's MFMAs follow the barrier and cover the next slab's first
-// fragment reads.
+// every LDS address is one of a few per-lane registers plus an immediate. A
+// slab is two reduction steps of 32. Each slab issues the next slab's loads
+// into the other stage under the first half of its step 0, reads step 1's
+// fragments under step 0's MFMAs, and waits for its loads a quarter into step
+// 1 at the slab's one barrier; the rest of step 1's MFMAs follow the barrier
+// and cover the next slab's step-0 fragment reads.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int FM, int FN>
 __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, uint4* st1, int64_t row0,
                                                  int64_t col0, int lane, int wm, int wn,
-                                                 floatx16 (&acc)[FM][FN]) {
+                                                 floatx4 (&acc)[FM][FN]) {
     constexpr int WAVES = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr uint32_t kAStage = BM * kRowChunks * 16;                    // bytes
-    constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per sub-step
+    constexpr int kReads = FM * (A_KC ? 1 : 2) + FN * (B_KC ? 1 : 2);   // LDS reads per reduction step
     // With 8 waves, waves 0-3 (one per SIMD: a block's waves are dealt to the 4
     // SIMDs in turn) load the slabs and waves 4-7 only compute. A loading wave
     // stalls whenever the CU's vector-memory path is backed up; its partner's
-    // MFMAs keep the SIMD's matrix core busy meanwhile (4096^3: ~2% faster than
-    // every wave loading, and than 4 waves of 128 x 128). The loading waves run
+    // MFMAs keep the SIMD's matrix core busy meanwhile. The loading waves run
     // at a higher issue priority so that their loads go out as early as possible.
     constexpr int kLoadWaves = WAVES == 8 ? 4 : WAVES;
     using LA = DmaLoader<BM, kLoadWaves, A_KC>;
     using LB = DmaLoader<BN, kLoadWaves, B_KC>;
     constexpr int kLoads = LA::kPer + LB::kPer;                          // loads per loading wave per slab
-    constexpr int kMfma = FM * FN;                                       // MFMAs per sub-step
-    static_assert(FM == 4 && (FN == 4 || FN == 2) && WTM == 32 * FM && WTN == 32 * FN, "4 x 4 or 4 x 2 blocks per wave");
-    static_assert(kReads <= 2 * kMfma && kLoads <= 2 * kMfma, "reads and loads fit the sub-steps");
+    constexpr int kMfma = FM * FN;                                       // MFMAs per reduction step
+    // Step 1's MFMAs before the barrier; the rest (three quarters) leave time
+    // for the next slab's step-0 reads after it.
+    constexpr int kPre = kMfma / 4;
+    static_assert(FM == 8 && FN == 4 && WTM == 16 * FM && WTN == 16 * FN, "8 x 4 blocks of 16 x 16 per wave");
+    static_assert(kLoads <= kMfma && kReads <= kMfma, "loads and reads fit step 0");
     static_assert(kAStage <= 32768 && BN * kRowChunks * 16 <= 32768, "fragment offsets must fit the LDS immediate");
     const int nk = int(g.R / kBK);
     typedef __attribute__((address_space(3))) uint8_t lds8;
@@ -416,8 +385,8 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     LB lb;
     la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, wave % kLoadWaves, lane);
     lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, wave % kLoadWaves, lane);
-    FragAddr<BM, A_KC> fa;
-    FragAddr<BN, B_KC> fb;
+    FragAddr<BM, A_KC, FM> fa;
+    FragAddr<BN, B_KC, FN> fb;
     fa.init(wm * WTM, lane, 0);
     fb.init(wn * WTN, lane, kAStage);
     // byte offset of slab kt within a panel: 64 elements along a KC row, 64 rows of an MN panel
@@ -427,74 +396,79 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
         la.fetch(s8[stage], uint32_t(kt) * a_step);
         lb.fetch(s8[stage] + kAStage, uint32_t(kt) * b_step);
     };
-    // in the order the MFMAs consume them (A row block 0 with every B block
-    // first), so the first MFMA of a sub-step waits for two reads, not five
-    auto read_frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
-        af[0] = fa.read(s8[stage], 0, kk, 0);
+    // Step 1's fragments, read under step 0's MFMAs: B's first (every MFMA of
+    // step 0 still uses its own), then A's in the order step 0 retires its
+    // blocks.
+    auto read_ba = [&](int stage, int ks, half8 (&af)[FM], half8 (&bf)[FN]) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[j] = fb.read(s8[stage], j, kk, 0);
+        for (int j = 0; j < FN; ++j) bf[j] = fb.read(s8[stage], j, ks, 0);
 #pragma unroll
-        for (int i = 1; i < FM; ++i) af[i] = fa.read(s8[stage], i, kk, 0);
+        for (int i = 0; i < FM; ++i) af[i] = fa.read(s8[stage], i, ks, 0);
     };
+    // The next slab's step-0 fragments, in the order its MFMAs consume them (A
+    // block 0 with every B block first).
+    auto read_ab = [&](int stage, int ks, half8 (&af)[FM], half8 (&bf)[FN]) {
+        af[0] = fa.read(s8[stage], 0, ks, 0);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = fb.read(s8[stage], j, ks, 0);
+#pragma unroll
+        for (int i = 1; i < FM; ++i) af[i] = fa.read(s8[stage], i, ks, 0);
+    };
+    // block (i, j) = (t / FN, t % FN): B's fragment first, so lane l of block
+    // (i, j) accumulates output row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3
     auto mfma = [&](const half8 (&af)[FM], const half8 (&bf)[FN], int from, int to) {
 #pragma unroll
         for (int t = from; t < to; ++t)
-            acc[t / FN][t % FN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[t % FN], af[t / FN], acc[t / FN][t % FN], 0, 0, 0);
+            acc[t / FN][t % FN] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[t % FN], af[t / FN], acc[t / FN][t % FN], 0, 0, 0);
     };
     // vmcnt(0), expcnt and lgkmcnt left at their maxima: this wave's loads into LDS have landed
     auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     half8 af[2][FM], bf[2][FN];
-    // Prologue: slab 0 in stage 0, and its first fragments.
+    // Prologue: slab 0 in stage 0, and its step-0 fragments.
     if (loader) fetch(0, 0);
     wait_loads();
     __syncthreads();
-    read_frags(0, 0, af[0], bf[0]);
+    read_ab(0, 0, af[0], bf[0]);
 
     // One slab in stage S; a loading wave (LD) loads its share of the next slab
-    // (or, after the last, a copy of it) into the other stage. Sub-steps 0-2
-    // read the following sub-step's fragments under their MFMAs; then the
-    // slab's one barrier, after which the next slab has landed in the other
-    // stage and every read of stage S is done (sub-step 3's fragments were read
-    // before it), so sub-step 3's MFMAs run with the next slab's first
-    // fragments read beneath them.
+    // (or, after the last, a copy of it) into the other stage. At the slab's
+    // one barrier the next slab has landed in the other stage and every read of
+    // stage S is done (all of step 1's fragments were read before it).
     auto slab = [&](int kt, auto s_tag, auto ld_tag) {
         constexpr int S = decltype(s_tag)::value;
         constexpr bool LD = decltype(ld_tag)::value;
         if constexpr (LD) fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
+        read_ba(S, 1, af[1], bf[1]);
+        mfma(af[0], bf[0], 0, kMfma);
+        mfma(af[1], bf[1], 0, kPre);
+        // Instruction order (groups are filled in program order): step 0's
+        // MFMAs, each followed (in a loading wave, over the first kLoads) by one
+        // load of the next slab and by its even share of step 1's fragment
+        // reads; then step 1's first kPre MFMAs.
 #pragma unroll
-        for (int kk = 0; kk < 3; ++kk) {
-            read_frags(S, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
-            mfma(af[kk & 1], bf[kk & 1], 0, kMfma);
+        for (int m = 0; m < kMfma; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (LD && m < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            const int nr = (m + 1) * kReads / kMfma - m * kReads / kMfma;
+#pragma unroll
+            for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        // Instruction order (groups are filled in program order): each MFMA
-        // followed by the next sub-step's fragment reads (one after each of the
-        // first MFMAs with 16 per sub-step, spread evenly with 8) and, in a
-        // loading wave, loads of the next slab spread over sub-steps 0 and 1
-        // (after every MFMA when a wave loads more blocks than a sub-step has
-        // MFMAs, else after every other one).
-        for (int kk = 0; kk < 3; ++kk)
-            for (int m = 0; m < kMfma; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (LD && kLoads <= kMfma && kk < 2 && !(m & 1) && kk * (kMfma / 2) + m / 2 < kLoads)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                if (LD && kLoads > kMfma && kk < 2 && kk * kMfma + m < kLoads)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                const int nr = kMfma == 16 ? int(m < kReads) : (m + 1) * kReads / kMfma - m * kReads / kMfma;
-                for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        // The barrier stays exactly here: without the fences the scheduler
-        // moves sub-step 3's MFMAs below it, where they no longer cover the next
-        // slab's first reads.
+#pragma unroll
+        for (int m = 0; m < kPre; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        // The barrier stays exactly here: the scheduler would otherwise move
+        // MFMAs across it.
         __builtin_amdgcn_sched_barrier(0);
         wait_loads();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(S ^ 1, 0, af[0], bf[0]);
-        mfma(af[1], bf[1], 0, kMfma);
-        for (int m = 0; m < kMfma; ++m) {
+        read_ab(S ^ 1, 0, af[0], bf[0]);
+        mfma(af[1], bf[1], kPre, kMfma);
+#pragma unroll
+        for (int m = 0; m < kMfma - kPre; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            const int nr = kMfma == 16 ? int(m < kReads) : (m + 1) * kReads / kMfma - m * kReads / kMfma;
+            const int nr = (m + 1) * kReads / (kMfma - kPre) - m * kReads / (kMfma - kPre);
+#pragma unroll
             for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
@@ -543,12 +517,12 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return uin
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int EPI, int KIND>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArgs g) {
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int FM = WTM / 16, FN = WTN / 16;            // 16 x 16 MFMA blocks per wave
     constexpr int kStage = (BM + BN) * kRowChunks;         // uint4 per LDS stage
     // the two stages of the reduction loop, as two variables (see reduce_tile_pipe)
     __shared__ uint4 lds0[kStage];
     __shared__ uint4 lds1[kStage];
-    static_assert(BM % 32 == 0 && BN % 32 == 0, "tile must be whole MFMA tiles");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles must be whole pairs of MFMA blocks");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -567,13 +541,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
     const int tn = (lb % per_group) / gsize;
     const int64_t row0 = int64_t(tm) * BM, col0 = int64_t(tn) * BN;
 
-    floatx16 acc[FM][FN];
+    floatx4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
     const bool full = g.a_vec && g.b_vec && (g.R % kBK) == 0 && row0 + BM <= g.Mc &&
                       col0 + BN <= g.Nc;
@@ -594,31 +568,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
 
     // ---- epilogue. The MFMA takes B's fragment as its first operand, so the
     // accumulator of block (i, j) holds the transposed tile: lane l has output
-    // row m = 32 i + (l & 31) and, in register r, column n = 32 j + 8 (r / 4) +
-    // 4 (l / 32) + r % 4 (wave-local), i.e. four consecutive columns of one row
-    // per group of four registers.
+    // row m = 16 i + (l & 15) and, in register r, column n = 16 j + 4 (l / 16) + r
+    // (wave-local), i.e. four consecutive columns of one row.
     const int64_t wrow0 = row0 + wm * WTM, wcol0 = col0 + wn * WTN;
     if (EPI == kEpiF32) {
         float* C = static_cast<float*>(g.C);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
+                const int64_t gr = wrow0 + i * 16 + (lane & 15);
+                const int64_t gc = wcol0 + j * 16 + 4 * (lane >> 4);
+                if (gr >= g.Mc) continue;
+                float* dst = C + gr * g.ldc + gc;
+                if (g.c_vec && gc + 4 <= g.Nc) {
+                    *reinterpret_cast<mp::f32x4*>(dst) = mp::f32x4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t gr = wrow0 + i * 32 + (lane & 31);
-                    const int64_t gc = wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
-                    if (gr >= g.Mc) continue;
-                    float* dst = C + gr * g.ldc + gc;
-                    if (g.c_vec && gc + 4 <= g.Nc) {
-                        *reinterpret_cast<mp::f32x4*>(dst) =
-                            mp::f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (gc + e < g.Nc) dst[e] = acc[i][j][4 * q + e];
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (gc + e < g.Nc) dst[e] = acc[i][j][e];
                 }
+            }
         return;
     }
     // Binary16 out, staged through LDS (free once the reduction has ended): each
@@ -657,16 +627,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmArg
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = i * 32 + (lane & 31);
-                const int c = (j * 32 + 8 * q) / 8;            // chunk of the 8 columns 32 j + 8 q ..
-                const uint2 v = make_uint2(mp::f2h2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                           mp::f2h2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-                *reinterpret_cast<uint2*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16 +
-                                          8 * (lane >> 5)) = v;
-            }
+        for (int j = 0; j < FN; ++j) {
+            const int m = i * 16 + (lane & 15);
+            const int c = 2 * j + (lane >> 5);             // chunk of the 8 columns 16 j + 8 (l / 32) ..
+            const uint2 v = make_uint2(mp::f2h2(acc[i][j][0], acc[i][j][1]), mp::f2h2(acc[i][j][2], acc[i][j][3]));
+            *reinterpret_cast<uint2*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16 + 8 * ((lane >> 4) & 1)) = v;
+        }
     __syncthreads();
     auto staged = [&](int m, int c) {
         return *reinterpret_cast<const uint4*>(stage + (m * kChunks + (c ^ (m & (kChunks - 1)))) * 16);
