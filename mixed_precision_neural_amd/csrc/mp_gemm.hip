@@ -348,10 +348,10 @@ struct FragAddr {
 // only where this code says so. The loop is unrolled over the two stages, so
 // every LDS address is one of a few per-lane registers plus an immediate. A
 // slab is two reduction steps of 32. Each slab issues the next slab's loads
-// into the other stage under the first half of its step 0, reads step 1's
-// fragments under step 0's MFMAs, and waits for its loads a quarter into step
-// 1 at the slab's one barrier; the rest of step 1's MFMAs follow the barrier
-// and cover the next slab's step-0 fragment reads.
+// into the other stage under its step 0, reads step 1's fragments under step
+// 0's MFMAs, and waits for its loads half way into step 1 at the slab's one
+// barrier; the rest of step 1's MFMAs follow the barrier and cover the next
+// slab's step-0 fragment reads.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KC, bool B_KC, int FM, int FN>
 __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, uint4* st1, int64_t row0,
                                                  int64_t col0, int lane, int wm, int wn,
@@ -370,21 +370,18 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     using LB = DmaLoader<BN, kLoadWaves, B_KC>;
     constexpr int kLoads = LA::kPer + LB::kPer;                          // loads per loading wave per slab
     constexpr int kMfma = FM * FN;                                       // MFMAs per reduction step
-    // Step 1's MFMAs before the barrier; the rest (three quarters) leave time
-    // for the next slab's step-0 reads after it.
-    constexpr int kPre = kMfma / 4;
+    // Step 1's MFMAs before the barrier (half): the loads, issued under step 0,
+    // get 32 MFMAs before their wait; the other half of step 1 covers the next
+    // slab's step-0 reads.
+    constexpr int kPre = kMfma / 2;
     static_assert(FM == 8 && FN == 4 && WTM == 16 * FM && WTN == 16 * FN, "8 x 4 blocks of 16 x 16 per wave");
-    static_assert(kLoads <= kMfma && kReads <= kMfma, "loads and reads fit step 0");
+    static_assert(2 * kLoads <= kMfma && kReads <= kMfma, "loads and reads fit step 0");
     static_assert(kAStage <= 32768 && BN * kRowChunks * 16 <= 32768, "fragment offsets must fit the LDS immediate");
     const int nk = int(g.R / kBK);
     typedef __attribute__((address_space(3))) uint8_t lds8;
     lds8* s8[2] = {(lds8*)st0, (lds8*)st1};
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const bool loader = wave < kLoadWaves;
-    LA la;
-    LB lb;
-    la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, wave % kLoadWaves, lane);
-    lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, wave % kLoadWaves, lane);
     FragAddr<BM, A_KC, FM> fa;
     FragAddr<BN, B_KC, FN> fb;
     fa.init(wm * WTM, lane, 0);
@@ -392,10 +389,6 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     // byte offset of slab kt within a panel: 64 elements along a KC row, 64 rows of an MN panel
     const uint32_t a_step = A_KC ? 2 * kBK : uint32_t(2 * kBK * g.lda);
     const uint32_t b_step = B_KC ? 2 * kBK : uint32_t(2 * kBK * g.ldb);
-    auto fetch = [&](int kt, int stage) {
-        la.fetch(s8[stage], uint32_t(kt) * a_step);
-        lb.fetch(s8[stage] + kAStage, uint32_t(kt) * b_step);
-    };
     // Step 1's fragments, read under step 0's MFMAs: B's first (every MFMA of
     // step 0 still uses its own), then A's in the order step 0 retires its
     // blocks.
@@ -425,74 +418,83 @@ __device__ __forceinline__ void reduce_tile_pipe(const GemmArgs& g, uint4* st0, 
     auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     half8 af[2][FM], bf[2][FN];
-    // Prologue: slab 0 in stage 0, and its step-0 fragments.
-    if (loader) fetch(0, 0);
-    wait_loads();
-    __syncthreads();
-    read_ab(0, 0, af[0], bf[0]);
-
-    // One slab in stage S; a loading wave (LD) loads its share of the next slab
-    // (or, after the last, a copy of it) into the other stage. At the slab's
-    // one barrier the next slab has landed in the other stage and every read of
-    // stage S is done (all of step 1's fragments were read before it).
-    auto slab = [&](int kt, auto s_tag, auto ld_tag) {
-        constexpr int S = decltype(s_tag)::value;
+    // The whole loop, for loading (LD) and computing waves. Only a loading wave
+    // builds its loaders, so a computing wave holds none of their registers.
+    auto run = [&](auto ld_tag) {
         constexpr bool LD = decltype(ld_tag)::value;
-        if constexpr (LD) fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
-        read_ba(S, 1, af[1], bf[1]);
-        mfma(af[0], bf[0], 0, kMfma);
-        mfma(af[1], bf[1], 0, kPre);
-        // Instruction order (groups are filled in program order): step 0's
-        // MFMAs, each followed (in a loading wave, over the first kLoads) by one
-        // load of the next slab and by its even share of step 1's fragment
-        // reads; then step 1's first kPre MFMAs.
-#pragma unroll
-        for (int m = 0; m < kMfma; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (LD && m < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            const int nr = (m + 1) * kReads / kMfma - m * kReads / kMfma;
-#pragma unroll
-            for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        LA la;
+        LB lb;
+        if constexpr (LD) {
+            la.init(A_KC ? g.A + row0 * g.lda : g.A + row0, g.lda, wave % kLoadWaves, lane);
+            lb.init(B_KC ? g.B + col0 * g.ldb : g.B + col0, g.ldb, wave % kLoadWaves, lane);
         }
-#pragma unroll
-        for (int m = 0; m < kPre; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        // The barrier stays exactly here: the scheduler would otherwise move
-        // MFMAs across it.
-        __builtin_amdgcn_sched_barrier(0);
+        auto fetch = [&](int kt, int stage) {
+            la.fetch(s8[stage], uint32_t(kt) * a_step);
+            lb.fetch(s8[stage] + kAStage, uint32_t(kt) * b_step);
+        };
+        // Prologue: slab 0 in stage 0, and its step-0 fragments.
+        if constexpr (LD) fetch(0, 0);
         wait_loads();
         __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        read_ab(S ^ 1, 0, af[0], bf[0]);
-        mfma(af[1], bf[1], kPre, kMfma);
+        read_ab(0, 0, af[0], bf[0]);
+
+        // One slab in stage S; a loading wave loads its share of the next slab
+        // (or, after the last, a copy of it) into the other stage. At the slab's
+        // one barrier the next slab has landed in the other stage and every read
+        // of stage S is done (all of step 1's fragments were read before it).
+        auto slab = [&](int kt, auto s_tag) {
+            constexpr int S = decltype(s_tag)::value;
+            if constexpr (LD) fetch(kt + 1 < nk ? kt + 1 : kt, S ^ 1);
+            read_ba(S, 1, af[1], bf[1]);
+            mfma(af[0], bf[0], 0, kMfma);
+            mfma(af[1], bf[1], 0, kPre);
+            // Instruction order (groups are filled in program order): step 0's
+            // MFMAs, each followed by its even share of step 1's fragment reads
+            // and, in a loading wave, every other one by a load of the next slab;
+            // then step 1's first kPre MFMAs.
 #pragma unroll
-        for (int m = 0; m < kMfma - kPre; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            const int nr = (m + 1) * kReads / (kMfma - kPre) - m * kReads / (kMfma - kPre);
+            for (int m = 0; m < kMfma; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (LD && !(m & 1) && m / 2 < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                const int nr = (m + 1) * kReads / kMfma - m * kReads / kMfma;
 #pragma unroll
-            for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int m = 0; m < kPre; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            // The barrier stays exactly here: the scheduler would otherwise move
+            // MFMAs across it.
+            __builtin_amdgcn_sched_barrier(0);
+            wait_loads();
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            read_ab(S ^ 1, 0, af[0], bf[0]);
+            mfma(af[1], bf[1], kPre, kMfma);
+#pragma unroll
+            for (int m = 0; m < kMfma - kPre; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                const int nr = (m + 1) * kReads / (kMfma - kPre) - m * kReads / (kMfma - kPre);
+#pragma unroll
+                for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        };
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        // nk is even here. One loop body for every slab: after the last slab the
+        // "next" load re-reads that slab into the idle stage (1/nk extra loads),
+        // which keeps the loop free of tail copies. Every wave passes one barrier
+        // per slab.
+        if constexpr (LD) __builtin_amdgcn_s_setprio(2);
+        for (int kt = 0; kt < nk; kt += 2) {
+            slab(kt, C0());
+            slab(kt + 1, C1());
         }
+        if constexpr (LD) __builtin_amdgcn_s_setprio(0);
     };
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    using Load = std::integral_constant<bool, true>;
-    using NoLoad = std::integral_constant<bool, false>;
-    // nk is even here. One loop body for every slab: after the last slab the
-    // "next" load re-reads that slab into the idle stage (1/nk extra loads),
-    // which keeps the loop free of tail copies. Every wave passes one barrier
-    // per slab in either loop.
-    if (loader) {
-        __builtin_amdgcn_s_setprio(2);
-        for (int kt = 0; kt < nk; kt += 2) {
-            slab(kt, C0(), Load());
-            slab(kt + 1, C1(), Load());
-        }
-        __builtin_amdgcn_s_setprio(0);
-    } else {
-        for (int kt = 0; kt < nk; kt += 2) {
-            slab(kt, C0(), NoLoad());
-            slab(kt + 1, C1(), NoLoad());
-        }
-    }
+    if (loader)
+        run(std::integral_constant<bool, true>());
+    else
+        run(std::integral_constant<bool, false>());
     // The last slab read its (unused) successor's first fragments from the
     // idle stage; the epilogue stages the output through both stages.
     __syncthreads();
