@@ -89,3 +89,45 @@ def test_bn_apply_uses_correctly_rounded_sqrt_and_division(tmp_path):
     for sym, body in apply.items():
         assert "v_sqrt_f32" in body and re.search(r"v_fma_f32 v\d+, -v\d+, v\d+, v\d+", body), sym
         assert "v_div_fixup_f32" in body and "v_div_fmas_f32" in body, sym
+
+
+def back_edge_loops(body):
+    """Bodies of the loops in one kernel's assembly: the lines from a label to a branch
+    back to it."""
+    lines = body.splitlines()
+    labels = {}
+    for i, line in enumerate(lines):
+        m = re.match(r"^(\.LBB\w+):", line)
+        if m:
+            labels[m.group(1)] = i
+    loops = []
+    for i, line in enumerate(lines):
+        m = re.search(r"s_c?branch\w* (\.LBB\w+)", line)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            loops.append("\n".join(lines[labels[m.group(1)]:i]))
+    return loops
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_pipelined_gemm_loops_use_16x16x32_and_no_scratch(tmp_path):
+    """The 256 x 256 kernels issue only v_mfma_f32_16x16x32_f16. In every kernel with a
+    binary16 output (the ones the training step runs; FP32 output serves tests), neither
+    pipelined loop (128 MFMAs per pass) touches scratch memory, and the forward and dgrad
+    layouts (reduction-contiguous A) spill nothing at all. (Register spills of the
+    computing waves once cost 5-15 MiB of scratch traffic per launch.)"""
+    bodies = kernel_bodies(device_asm("mp_gemm", tmp_path))
+    big = {k: v for k, v in bodies.items() if "gemm_kernel" in k and "ILi256ELi256ELi2ELi4E" in k}
+    assert len(big) >= 10
+    for name, body in big.items():
+        m = re.search(r"ILi256ELi256ELi2ELi4ELb(\d)ELb(\d)ELi(\d)ELi(\d)E", name)
+        a_kc, epi = m.group(1) == "1", int(m.group(3))
+        mfmas = set(re.findall(r"v_mfma_\w+", body))
+        assert mfmas == {"v_mfma_f32_16x16x32_f16"}, (name, mfmas)
+        pipelined = [lp for lp in back_edge_loops(body) if lp.count("v_mfma_") == 128]
+        assert len(pipelined) == 2, name                    # the loading and the computing waves' loop
+        if epi == 0:
+            continue
+        for lp in pipelined:
+            assert "scratch_" not in lp, name
+        if a_kc and epi != 0:
+            assert "scratch_" not in body, name
