@@ -318,17 +318,17 @@ def hbm_ceiling(torch, probe, gib: int = 4) -> dict:
     return out
 
 
-def mfma_clock(torch, probe, operands: int, blocks: int = 256, ms_target: float = 25.0) -> dict:
+def mfma_clock(torch, probe, operands: int, shape: int, blocks: int = 256, ms_target: float = 25.0) -> dict:
     """The shader clock and the MFMA rate under a pure binary16 matrix-core load (one block of four
-    waves per CU, eight independent v_mfma_f32_32x32x16_f16 chains per wave, sixteen MFMAs a round),
-    with near-constant operands (probe.CONSTANT) or random ones like a GEMM's (probe.RANDOM)."""
+    waves per CU, independent MFMA chains, 16 x 32768 FLOP a round) of the form `shape`, with
+    near-constant operands (probe.CONSTANT) or random ones like a GEMM's (probe.RANDOM)."""
     out_t = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda")
     iters = 1000
-    probe.mfma_clock(blocks, iters, out_t, operands)       # warm-up and sizing
-    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t, operands), 1)
+    probe.mfma_clock(blocks, iters, out_t, operands, shape)       # warm-up and sizing
+    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t, operands, shape), 1)
     iters = max(1000, int(iters * ms_target / max(ms, 1e-3)))
-    khz = probe.mfma_clock(blocks, iters, out_t, operands)
-    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t, operands), 1)
+    khz = probe.mfma_clock(blocks, iters, out_t, operands, shape)
+    ms = _event_avg_ms(torch, lambda: probe.mfma_clock(blocks, iters, out_t, operands, shape), 1)
     t = out_t.cpu().numpy().reshape(blocks, 4).astype("float64")
     mhz = (t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2]) * khz / 1000.0
     flop = blocks * 4 * iters * 16 * 2.0 * 32 * 32 * 16
@@ -338,7 +338,7 @@ def mfma_clock(torch, probe, operands: int, blocks: int = 256, ms_target: float 
             "mfma_f16_TFLOPs": round(tf, 1), "frac_of_spec": round(tf / PEAK_F16_TFLOPS, 4),
             "clock_adjusted_peak_TFLOPs": round(PEAK_F16_TFLOPS * mhz_med / 2400.0, 1),
             "kernel_ms": round(ms, 3), "realtime_khz": khz,
-            "load": f"{blocks} blocks x 4 waves, 8 independent MFMA chains per wave, {iters} rounds of 16"}
+            "load": f"{blocks} blocks x 4 waves, {iters} rounds of 16 x 32768 FLOP per wave"}
 
 
 def sweep_config(mp, torch, name, tensors, scale, hyper, inject, reps, copy_gbps) -> dict:
@@ -539,8 +539,8 @@ def roofline_line(dom: str, g: dict, random_operand_tflops: float) -> dict:
     """The roofline object of the dominant GEMM kind: achieved TFLOP/s against the 2.5 PFLOP/s FP16
     dense peak, the counter traffic, from the counter pass how busy the matrix cores were and the
     shader clock the chip ran this kernel at (the spec peak assumes 2.4 GHz), and the fraction of the
-    MFMA rate the chip sustains on random binary16 operands with no memory traffic at all (the
-    matrix-core probe measured in this run)."""
+    rate of the GEMMs' MFMA form (v_mfma_f32_16x16x32_f16) the chip sustains on random binary16
+    operands with no memory traffic at all (the matrix-core probe measured in this run)."""
     busy, mhz = measured_mfma(dom)
     out = {"bound": "mfma", "kernel": f"gemm_{dom}", "achieved": g["TFLOPs"], "peak": PEAK_F16_TFLOPS,
            "unit": "TFLOP/s", "frac": g["frac"], "traffic": measured_traffic("gemm", dom),
@@ -814,8 +814,9 @@ def main():
     from mixed_precision_neural_amd import probe
     c3 = c3_gemms(mp, torch)
     ceiling = hbm_ceiling(torch, probe)
-    clock = {"constant_operands": mfma_clock(torch, probe, probe.CONSTANT),
-             "random_operands": mfma_clock(torch, probe, probe.RANDOM)}
+    clock = {"v_mfma_f32_16x16x32_f16": {"constant_operands": mfma_clock(torch, probe, probe.CONSTANT, probe.MFMA_16X16X32),
+                                         "random_operands": mfma_clock(torch, probe, probe.RANDOM, probe.MFMA_16X16X32)},
+             "v_mfma_f32_32x32x16_f16": {"random_operands": mfma_clock(torch, probe, probe.RANDOM, probe.MFMA_32X32X16)}}
     copy_gbps = ceiling["copy"]["GBps"]
     c2 = c2_sweep(mp, torch, copy_gbps)
     c5 = c5_sweep(mp, torch, workloads, copy_gbps)
@@ -864,7 +865,7 @@ def main():
                             "recompute": "in the GEMM epilogues, GELU'(Z) evaluated in the backward",
                             "separate": "separate point-wise kernels"}[model.gelu],
                    "loss_multiplier_c": c},
-        "roofline": roofline_line(dom, gemm[dom], clock["random_operands"]["mfma_f16_TFLOPs"]),
+        "roofline": roofline_line(dom, gemm[dom], clock["v_mfma_f32_16x16x32_f16"]["random_operands"]["mfma_f16_TFLOPs"]),
         "gemm": gemm,
         "mp_step": {"bound": "hbm", "mode": "flag from the wgrad epilogues, one update pass",
                     "avg_us": round(sweep_ms * 1e3, 2),

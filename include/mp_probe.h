@@ -51,21 +51,26 @@ typedef enum {
                                         sixteen different registers per wave in rotation       */
 } mp_probe_operands;
 
+typedef enum {
+    MP_PROBE_MFMA_32X32X16 = 0,      /* v_mfma_f32_32x32x16_f16, eight accumulator chains per wave  */
+    MP_PROBE_MFMA_16X16X32 = 1       /* v_mfma_f32_16x16x32_f16 (the GEMMs' form), sixteen chains   */
+} mp_probe_mfma_shape;
+
 /* Runs `blocks` blocks of four waves; every wave issues `iters` rounds of
- * sixteen v_mfma_f32_32x32x16_f16 (binary16 inputs, FP32 sums) on eight
- * independent chains, i.e. 16 * 32768 FLOP per round, with operands of the
- * kind `operands` names. The matrix cores' power draw, and so the clock the
- * chip holds, depends on how many operand bits change between MFMAs: the
- * CONSTANT load shows the clock ceiling, the RANDOM load the MFMA rate the
- * chip sustains on data like a GEMM's. Wave 0 of each block records its shader
- * clock counter (s_memtime) and the constant-rate counter (s_memrealtime)
- * before and after the loop: out[4 b + 0..3] = {clock start, clock end, real
- * start, real end} (device uint64, 4 * blocks entries). *realtime_khz (host)
- * receives the constant counter's rate. The shader clock in MHz under this
- * load is (clock end - start) / (real end - start) * realtime_khz / 1000.
+ * 16 * 32768 FLOP of binary16 MFMAs with FP32 sums, of the form `shape`, on
+ * independent chains, with operands of the kind `operands`. The matrix
+ * cores' power draw, and so the clock the chip holds, depends on the MFMA
+ * form and on how many operand bits change between MFMAs: the CONSTANT load
+ * shows the clock ceiling, the RANDOM load the MFMA rate the chip sustains on
+ * data like a GEMM's. Wave 0 of each block records its shader clock counter
+ * (s_memtime) and the constant-rate counter (s_memrealtime) before and after
+ * the loop: out[4 b + 0..3] = {clock start, clock end, real start, real end}
+ * (device uint64, 4 * blocks entries). *realtime_khz (host) receives the
+ * constant counter's rate. The shader clock in MHz under this load is
+ * (clock end - start) / (real end - start) * realtime_khz / 1000.
  * Errors: MP_ERR_INVALID_ARGUMENT (blocks < 1, iters < 1, unknown operand
- * kind, null pointers), MP_ERR_HIP. */
-mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, int32_t operands, uint64_t* out,
+ * kind or shape, null pointers), MP_ERR_HIP. */
+mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, int32_t operands, int32_t shape, uint64_t* out,
                               int32_t* realtime_khz, mp_stream stream);
 
 #ifdef __cplusplus

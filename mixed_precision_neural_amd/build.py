@@ -24,6 +24,10 @@ PROBE_LIB = os.path.join(HERE, "libmp_probe.so")
 SOURCES = ["mp_common.hip", "mp_step.hip", "mp_gemm.hip", "mp_aux.hip", "mp_stats.hip", "mp_reduce.hip",
            "mp_noalloc.hip"]
 PROBE_SOURCES = ["mp_probe.hip"]
+# Per-source flags. The matrix-core probe keeps its MFMA accumulators in VGPRs: with the
+# compiler's default (AGPRs for a kernel of one block per CU) it shuffled the 16x16x32
+# accumulators between register files around every MFMA and could not issue back to back.
+SOURCE_FLAGS = {"mp_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,7 +42,7 @@ FLAGS = [
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -17,6 +17,7 @@ constexpr int64_t kBlockVecs = int64_t(kThreads) * kPer;   // 16 KiB per block a
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <bool NT>
 __device__ __forceinline__ mp::u32x4 ld(const mp::u32x4* p) {
@@ -89,15 +90,17 @@ __device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
     return x;
 }
 
-// Eight independent accumulator chains per wave keep the matrix core issuing
-// back to back with one wave per SIMD; a round is sixteen MFMAs, two on each
-// chain, taking operand pair (a[j], b[j + 3]) then (a[j + 5], b[j]) (indices
-// mod 8). CONSTANT: all eight A and B registers hold the same few small
-// multiples of 2^-8 (almost no bits change between MFMAs). RANDOM: each of the
-// sixteen registers holds its own random binary16 values (random sign and
-// 10-bit mantissa, exponent 2^-3 .. 2^0, like unit-scale activations and
-// weights), so consecutive MFMAs see unrelated operands, as in a GEMM.
-template <int OPERANDS>
+// Independent accumulator chains keep the matrix core issuing back to back with
+// one wave per SIMD. A round is 16 x 32768 FLOP on eight chains of
+// v_mfma_f32_32x32x16_f16 (two MFMAs each: operand pairs (a[j], b[j + 3]) then
+// (a[j + 5], b[j]), indices mod 8), or on sixteen chains of
+// v_mfma_f32_16x16x32_f16 (two each: (a[j mod 8], b[(j + 3 + j / 8) mod 8]) then
+// (a[j + 5], b[j]), mod 8). CONSTANT: all eight A and B registers hold the same
+// few small multiples of 2^-8 (almost no bits change between MFMAs). RANDOM:
+// each of the sixteen registers holds its own random binary16 values (random
+// sign and 10-bit mantissa, exponent 2^-3 .. 2^0, like unit-scale activations
+// and weights), so consecutive MFMAs see unrelated operands, as in a GEMM.
+template <int OPERANDS, int SHAPE>
 __global__ __launch_bounds__(kThreads) void mfma_clock_kernel(int iters, uint64_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const uint32_t seed = probe_hash(uint32_t(blockIdx.x) * kThreads + threadIdx.x + 1u);
@@ -115,26 +118,48 @@ __global__ __launch_bounds__(kThreads) void mfma_clock_kernel(int iters, uint64_
                 b[p][i] = __builtin_bit_cast(_Float16, uint16_t((yb & 0x83FFu) | ((0xCu + ((yb >> 10) & 3u)) << 10)));
             }
         }
-    floatx16 acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-    const uint64_t c0 = __builtin_amdgcn_s_memtime();
-    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-    for (int i = 0; i < iters; ++i) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[(j + 3) & 7], acc[j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[(j + 5) & 7], b[j], acc[j], 0, 0, 0);
-    }
     float s = 0.0f;
+    uint64_t c0, c1, r0, r1;
+    if constexpr (SHAPE == MP_PROBE_MFMA_32X32X16) {
+        floatx16 acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += acc[j][r];
-    const uint64_t c1 = __builtin_amdgcn_s_memtime();
-    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+            for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+        for (int i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[(j + 3) & 7], acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[(j + 5) & 7], b[j], acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += acc[j][r];
+    } else {
+        floatx4 acc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][r] = 0.0f;
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+        for (int i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j & 7], b[(j + 3 + (j >> 3)) & 7], acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[(j + 5) & 7], b[j & 7], acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s += acc[j][r];
+    }
+    c1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
     if (threadIdx.x == 0) {
         uint64_t* o = out + 4 * int64_t(blockIdx.x);
         o[0] = c0;
@@ -173,18 +198,26 @@ extern "C" mp_status mp_probe_hbm(int32_t mode, const void* src, void* dst, size
     return mp::launch_status("mp_probe_hbm");
 }
 
-extern "C" mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, int32_t operands, uint64_t* out,
-                                         int32_t* realtime_khz, mp_stream stream) {
+extern "C" mp_status mp_probe_mfma_clock(int32_t blocks, int32_t iters, int32_t operands, int32_t shape,
+                                         uint64_t* out, int32_t* realtime_khz, mp_stream stream) {
     if (blocks < 1 || iters < 1 || !out || !realtime_khz) return MP_ERR_INVALID_ARGUMENT;
     if (operands != MP_PROBE_OPERANDS_CONSTANT && operands != MP_PROBE_OPERANDS_RANDOM) return MP_ERR_INVALID_ARGUMENT;
+    if (shape != MP_PROBE_MFMA_32X32X16 && shape != MP_PROBE_MFMA_16X16X32) return MP_ERR_INVALID_ARGUMENT;
     int dev = 0, khz = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
     if (e != hipSuccess) return mp::hip_status(e, "mp_probe_mfma_clock");
     *realtime_khz = khz;
-    if (operands == MP_PROBE_OPERANDS_CONSTANT)
-        mfma_clock_kernel<MP_PROBE_OPERANDS_CONSTANT><<<uint32_t(blocks), kThreads, 0, mp::as_stream(stream)>>>(iters, out);
-    else
-        mfma_clock_kernel<MP_PROBE_OPERANDS_RANDOM><<<uint32_t(blocks), kThreads, 0, mp::as_stream(stream)>>>(iters, out);
+    const dim3 g{uint32_t(blocks)};
+    auto st = mp::as_stream(stream);
+    constexpr int kC = MP_PROBE_OPERANDS_CONSTANT, kR = MP_PROBE_OPERANDS_RANDOM;
+    constexpr int k32 = MP_PROBE_MFMA_32X32X16, k16 = MP_PROBE_MFMA_16X16X32;
+    if (shape == k32) {
+        if (operands == kC) mfma_clock_kernel<kC, k32><<<g, kThreads, 0, st>>>(iters, out);
+        else mfma_clock_kernel<kR, k32><<<g, kThreads, 0, st>>>(iters, out);
+    } else {
+        if (operands == kC) mfma_clock_kernel<kC, k16><<<g, kThreads, 0, st>>>(iters, out);
+        else mfma_clock_kernel<kR, k16><<<g, kThreads, 0, st>>>(iters, out);
+    }
     return mp::launch_status("mp_probe_mfma_clock");
 }

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmp_probe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mp_probe.h")
 READ, WRITE, COPY = 0, 1, 2
 CONSTANT, RANDOM = 0, 1      # operand kinds of the matrix-core probe
+MFMA_32X32X16, MFMA_16X16X32 = 0, 1   # its MFMA forms
 
 _lib = None
 
@@ -31,7 +32,7 @@ def lib() -> C.CDLL:
         vp, i32 = C.c_void_p, C.c_int32
         L.mp_probe_hbm.argtypes = [i32, vp, vp, C.c_size_t, i32, i32, vp]
         L.mp_probe_hbm.restype = C.c_int
-        L.mp_probe_mfma_clock.argtypes = [i32, i32, i32, vp, C.POINTER(i32), vp]
+        L.mp_probe_mfma_clock.argtypes = [i32, i32, i32, i32, vp, C.POINTER(i32), vp]
         L.mp_probe_mfma_clock.restype = C.c_int
         _lib = L
     return _lib
@@ -45,12 +46,14 @@ def hbm(mode: int, src: torch.Tensor | None, dst: torch.Tensor, nbytes: int, blo
                               _stream(stream)), "mp_probe_hbm")
 
 
-def mfma_clock(blocks: int, iters: int, out: torch.Tensor, operands: int = CONSTANT, stream=None) -> int:
-    """One launch of the matrix-core probe (operands: CONSTANT or RANDOM); out: int64 GPU tensor of
-    4 * blocks entries. Returns the constant counter's rate in kHz."""
+def mfma_clock(blocks: int, iters: int, out: torch.Tensor, operands: int = CONSTANT,
+               shape: int = MFMA_16X16X32, stream=None) -> int:
+    """One launch of the matrix-core probe (operands: CONSTANT or RANDOM; shape: MFMA_32X32X16 or
+    MFMA_16X16X32); out: int64 GPU tensor of 4 * blocks entries. Returns the constant counter's
+    rate in kHz."""
     if out.dtype != torch.int64 or out.numel() < 4 * blocks or not out.is_cuda:
         raise ValueError("out must be an int64 GPU tensor of 4 * blocks entries")
     khz = C.c_int32(0)
-    _check(lib().mp_probe_mfma_clock(int(blocks), int(iters), int(operands), C.c_void_p(out.data_ptr()),
+    _check(lib().mp_probe_mfma_clock(int(blocks), int(iters), int(operands), int(shape), C.c_void_p(out.data_ptr()),
                                      C.byref(khz), _stream(stream)), "mp_probe_mfma_clock")
     return int(khz.value)

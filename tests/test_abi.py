@@ -146,6 +146,8 @@ def test_probe_library_exports_and_validation():
     assert L.mp_probe_hbm(0, None, P, 4096, 0, 0, None) == INVALID       # read needs a source
     assert L.mp_probe_hbm(2, P, C.c_void_p(0x1008), 4096, 0, 0, None) == INVALID   # misaligned
     khz = C.c_int32()
-    assert L.mp_probe_mfma_clock(0, 10, probe.CONSTANT, P, C.byref(khz), None) == INVALID
-    assert L.mp_probe_mfma_clock(1, 10, probe.RANDOM, None, C.byref(khz), None) == INVALID
-    assert L.mp_probe_mfma_clock(1, 10, 2, P, C.byref(khz), None) == INVALID     # unknown operand kind
+    k16 = probe.MFMA_16X16X32
+    assert L.mp_probe_mfma_clock(0, 10, probe.CONSTANT, k16, P, C.byref(khz), None) == INVALID
+    assert L.mp_probe_mfma_clock(1, 10, probe.RANDOM, k16, None, C.byref(khz), None) == INVALID
+    assert L.mp_probe_mfma_clock(1, 10, 2, k16, P, C.byref(khz), None) == INVALID     # unknown operand kind
+    assert L.mp_probe_mfma_clock(1, 10, probe.RANDOM, 2, P, C.byref(khz), None) == INVALID   # unknown MFMA form
