@@ -113,6 +113,39 @@ def test_exact_integer_sums_direct_to_lds(M, N, K):
     assert np.array_equal(dw.astype(np.float64), (dYf.T @ Xf) * q2)
 
 
+def test_exact_integer_sums_direct_to_lds_padded_rows():
+    """P8 on the direct-to-LDS loop with row pitches above the row length (multiples of 8, so
+    the loop still applies): every operand and output a view into a wider buffer. At 4096 x
+    4096 x 2048 all three layers run the 256 x 256 loop; its slab offsets along the pitch (the
+    reduction-strided operands step 64 pitches per slab) and the binary16 outputs' row stores
+    must follow the pitch, and the columns past each row stay untouched. Binary16 outputs: the
+    exact sums rounded once to nearest even."""
+    require_gpu()
+    M, N, K, q = 4096, 4096, 2048, 4
+    rng = np.random.Generator(np.random.PCG64(17))
+    X, Xi = grid_bits(rng, (M, K + 24), -q)
+    W, Wi = grid_bits(rng, (N, K + 40), -q)
+    dY, dYi = grid_bits(rng, (M, N + 8), -q)
+    dX_, dW_, dY_ = dev_f16(X)[:, :K], dev_f16(W)[:, :K], dev_f16(dY)[:, :N]
+    fill = 0x7E00                                          # a NaN pattern no GEMM output can take
+    outs = {name: torch.from_numpy(np.full(shape, fill, np.uint16).view(np.int16)).cuda().view(torch.float16)
+            for name, shape in (("y", (M, N + 16)), ("dx", (M, K + 32)), ("dw", (N, K + 8)))}
+    mp.linear_fwd(dX_, dW_, Y=outs["y"][:, :N])
+    mp.linear_dgrad(dY_, dW_, dX=outs["dx"][:, :K])
+    mp.linear_wgrad(dY_, dX_, dW=outs["dw"][:, :K])
+    torch.cuda.synchronize()
+    Xf, Wf, dYf = (a.astype(np.float64) for a in (Xi[:, :K], Wi[:, :K], dYi[:, :N]))
+    q2 = 2.0 ** (-2 * q)
+    want = {"y": (Xf @ Wf.T) * q2, "dx": (dYf @ Wf) * q2, "dw": (dYf.T @ Xf) * q2}
+    for name, ref in want.items():
+        got = host_bits16(outs[name])
+        cols = ref.shape[1]
+        # the FP32 sums are exact (multiples of 2^-8 below 2^16), so the binary16 output is the
+        # nearest-even binary16 of the exact sum (numpy rounds float64 to float16 that way)
+        assert np.array_equal(got[:, :cols], ref.astype(np.float16).view(np.uint16)), name
+        assert (got[:, cols:] == fill).all(), name
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 512, 256), (64, 10, 512), (300, 520, 200), (777, 1000, 333),
                                    (2600, 3100, 96), (4099, 2050, 130), (512, 768, 256),
                                    (1280, 1024, 384)])
