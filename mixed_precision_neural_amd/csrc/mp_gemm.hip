@@ -71,7 +71,7 @@ struct GemmArgs {
     const uint16_t* Z;           // kEpiDact: saved pre-activation; kEpiMul: saved act' (binary16), ldz
     int64_t ldc2, ldz;
     int aux_vec;                 // 16-byte access allowed for C2 / Z
-    int pipe_ok;                 // operand panels under 4 GB: the buffer-load main loop applies
+    int pipe_ok;                 // non-empty reduction, operand panels under 4 GB: the buffer-load main loop applies
     int tiles_m, tiles_n;
 };
 
@@ -726,7 +726,9 @@ mp_status launch_cfg(GemmArgs a, hipStream_t s, const char* name) {
         const int64_t bytes = kc ? (int64_t(BM > BN ? BM : BN) * ld + a.R) * 2 : (a.R + 64) * ld * 2 + 512;
         return bytes < (int64_t(1) << 32);
     };
-    a.pipe_ok = int(panel_ok(A_KC, a.lda) && panel_ok(B_KC, a.ldb) && a.R % (2 * kBK) == 0);
+    // The buffer-load loop fetches slab 0 before it looks at the reduction length: it needs a
+    // non-empty reduction (an empty one takes the general loop, which writes zeros).
+    a.pipe_ok = int(a.R > 0 && a.R % (2 * kBK) == 0 && panel_ok(A_KC, a.lda) && panel_ok(B_KC, a.ldb));
     const uint32_t blocks = uint32_t(a.tiles_m) * uint32_t(a.tiles_n);
     gemm_kernel<BM, BN, WM, WN, A_KC, B_KC, EPI, KIND><<<blocks, 64 * WM * WN, 0, s>>>(a);
     return mp::launch_status(name);

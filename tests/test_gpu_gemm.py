@@ -217,6 +217,36 @@ def test_strided_output_and_k_zero():
     assert (host_f32(z) == 0).all()                     # K = 0 writes zeros
 
 
+def test_empty_reduction_on_a_large_grid_writes_zeros():
+    """A zero-length reduction with an output of 128 or more 256 x 256 tiles must take the
+    general loop, which loads nothing, and write zeros. The operands are passed with row pitches
+    that allow 16-byte loads (a pitch of 8 for the empty rows, n for the empty row lists), so
+    that without the non-empty-reduction condition the launcher would pick the direct-to-LDS
+    loop, whose prologue fetches a first slab the empty operands do not have. Forward with
+    K = 0, dgrad with N = 0, wgrad with M = 0; binary16 and FP32 outputs, over a poisoned
+    output buffer."""
+    require_gpu()
+    n = 4096
+    no_cols = lambda: torch.empty((n, 8), dtype=torch.float16, device="cuda")[:, :0]   # [n, 0], pitch 8
+    no_rows = lambda: torch.empty((0, n), dtype=torch.float16, device="cuda")           # [0, n], pitch n
+    for dt in (torch.float16, torch.float32):
+        out = torch.full((n, n), float("nan"), dtype=dt, device="cuda")
+        mp.linear_fwd(no_cols(), no_cols(), Y=out)                     # K = 0
+        torch.cuda.synchronize()
+        assert (out == 0).all() and not torch.signbit(out).any()
+        out.fill_(float("nan"))
+        mp.linear_dgrad(no_cols(), no_rows(), dX=out)                  # N = 0
+        torch.cuda.synchronize()
+        assert (out == 0).all()
+        out.fill_(float("nan"))
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda") if dt == torch.float16 else None
+        mp.linear_wgrad(no_rows(), no_rows(), dW=out, found_inf=flag)  # M = 0
+        torch.cuda.synchronize()
+        assert (out == 0).all()
+        if flag is not None:
+            assert int(flag.item()) == 0
+
+
 def test_overflow_becomes_inf_and_sets_wgrad_flag():
     """binary16 outputs overflow to +-inf (never 65504); wgrad ORs the flag when asked."""
     require_gpu()
