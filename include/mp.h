@@ -378,11 +378,28 @@ size_t mp_softmax_workspace(int64_t rows, int64_t cols);
  * give 0, and a row of only -inf gives NaN. `workspace`: caller-owned device
  * memory of at least mp_softmax_workspace(rows, cols) bytes, 8-byte aligned,
  * overwritten. x and y may be the same matrix (ldx == ldy); no other overlap.
+ * Two forms, chosen per call from the sizes: when x and y are distinct,
+ * 16-byte aligned with pitches that are multiples of 8, and every row fits in
+ * at most 256 blocks of 204,800 values with the whole grid at most one block
+ * per compute unit, x is read once (each block keeps its segment on chip and
+ * exchanges its (max, sum) through the workspace); otherwise a two-pass form
+ * reads x twice. The result does not depend on timing, but the forms cut rows
+ * differently, so their outputs may differ in the last bit. Calls that share a
+ * workspace must not overlap.
  * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, rows > 2^31 - 1, ldx or ldy
  * < cols, a null pointer or too small a workspace when rows * cols > 0),
  * MP_ERR_HIP. */
 mp_status mp_softmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
                      void* workspace, size_t workspace_bytes, mp_stream stream);
+
+/* Tuning of mp_softmax's single-read form: how long, in microseconds, a block
+ * waits for the (max, sum) of its row's other blocks before computing the
+ * missing ones itself from x (default 200; at most 100000; 0: never wait,
+ * every block computes every other segment's pair). The wait ends either way,
+ * so a block that is not resident yet costs time, never progress, and every
+ * setting gives the same bits. Process-wide; applies to later calls. A
+ * negative value only queries. Returns the previous setting. */
+int64_t mp_softmax_wait_us(int64_t us);
 
 /* ------------------------------------------------------------------------
  * Auxiliary steps that a full training step needs around the hot path.

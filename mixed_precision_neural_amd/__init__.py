@@ -24,7 +24,7 @@ __all__ = [
     "Scaler", "ParamList", "step", "step_opt", "TensorList", "absmax", "scaler_init_from_absmax",
     "round_f32_to_f16", "act_fwd", "act_bwd", "loss_softmax_ce", "loss_mse",
     "loss_softmax_ce_workspace", "loss_mse_workspace", "loss_mse_noalloc",
-    "bn_stats", "bn_apply", "softmax",
+    "bn_stats", "bn_apply", "softmax", "softmax_wait_us",
     "MP_GRADS_PRECHECKED", "MP_CHECK_ONLY", "RELU", "GELU", "SGD", "NESTEROV", "ADAGRAD",
 ]
 
@@ -110,6 +110,8 @@ def lib() -> C.CDLL:
         L.mp_softmax_workspace.argtypes = [i64, i64]
         L.mp_softmax_workspace.restype = C.c_size_t
         L.mp_softmax.argtypes = [vp, i64, i64, i64, vp, i64, vp, C.c_size_t, vp]
+        L.mp_softmax_wait_us.argtypes = [i64]
+        L.mp_softmax_wait_us.restype = i64
         L.mp_status_string.argtypes = [C.c_int]
         L.mp_status_string.restype = C.c_char_p
         L.mp_last_hip_error.restype = C.c_char_p
@@ -508,6 +510,13 @@ def softmax(x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torc
     _check(lib().mp_softmax(px, rows, cols, ldx, py, ldy, C.c_void_p(ws.data_ptr()), nbytes,
                             _stream(stream)), "mp_softmax")
     return y
+
+
+def softmax_wait_us(us: int = -1) -> int:
+    """Sets how long (µs) a block of the single-read softmax waits for its row's other blocks
+    before computing their (max, sum) itself (0: never waits); negative only queries. Returns
+    the previous setting."""
+    return int(lib().mp_softmax_wait_us(int(us)))
 
 
 def _workspace(ws, nbytes: int, align: int, device) -> torch.Tensor:

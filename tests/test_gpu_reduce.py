@@ -147,11 +147,24 @@ def test_bn_apply_strided_and_in_place():
 
 
 # ---------------------------------------------------------------- softmax
-@pytest.mark.parametrize("rows,cols,ld", [(7, 10, 10), (1000, 512, 512), (3, 3 * 8192 + 5, 3 * 8192 + 8),
-                                          (2, 50000, 50001), (64, 793471, 793472)])
+SOFTMAX_SHAPES = [
+    (7, 10, 10),                 # element-wise two-pass form (odd pitch)
+    (1000, 512, 512),            # two-pass: more rows than blocks of the single-read form
+    (3, 3 * 8192 + 5, 3 * 8192 + 8),   # single read, one block per row, ragged tail
+    (2, 50000, 50001),           # element-wise two-pass form, several segments
+    (64, 793471, 793472),        # the page's vocabulary: single read, 4 blocks of 24,796 vectors per row
+    (5, 1200003, 1200008),       # single read, 37 blocks per row, registers only
+    (1, 40000005, 40000008),     # single read, 256 blocks, LDS in use, every lane polls 4 slots
+    (256, 204795, 204800),       # single read at capacity: one block per row, 25 vectors per thread
+    (257, 1000, 1000),           # one row too many for one block per compute unit: two-pass
+]
+
+
+@pytest.mark.parametrize("rows,cols,ld", SOFTMAX_SHAPES)
 def test_softmax_against_oracle(rows, cols, ld):
-    """One segment and several, a 16-byte path with a ragged tail and an element-wise path (odd
-    pitch), and the page's vocabulary size (64 rows of 793,471 with a row pitch of 793,472)."""
+    """Both forms (single read when the rows fit on chip, two-pass otherwise), 16-byte and
+    element-wise paths, ragged tails, the single-read form's capacity limit, and the page's
+    vocabulary size (64 rows of 793,471 with a row pitch of 793,472)."""
     require_gpu()
     rng = np.random.Generator(np.random.PCG64(rows + cols))
     x = (rng.standard_normal((rows, cols)) * 3.0).astype(np.float16).view(np.uint16)
@@ -163,6 +176,49 @@ def test_softmax_against_oracle(rows, cols, ld):
     ref = oracle.softmax(x)
     assert within_ulp(got, ref)
     assert np.array_equal(got, host_bits16(y2))
+
+
+@pytest.mark.parametrize("rows,cols,ld", [(64, 793471, 793472), (1, 40000005, 40000008), (5, 1200003, 1200008)])
+def test_softmax_single_read_without_waiting_gives_the_same_bits(rows, cols, ld):
+    """With the wait set to 0 every block computes its row's other segments' (max, sum) from x
+    itself: the path a block takes when the others are not resident. The bits must equal those
+    of the blocks exchanging their pairs."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(7 * rows + cols))
+    x = (rng.standard_normal((rows, cols)) * 3.0).astype(np.float16).view(np.uint16)
+    x[rows // 2, cols // 3] = 0x7BFF                          # one large value: a block's max
+    xd = padded(x, ld)
+    ref = host_bits16(mp.softmax(xd))
+    prev = mp.softmax_wait_us(0)
+    try:
+        got = host_bits16(mp.softmax(xd))
+    finally:
+        mp.softmax_wait_us(prev)
+    assert prev == mp.softmax_wait_us()
+    assert np.array_equal(got, ref)
+
+
+def test_softmax_concurrent_calls_on_two_streams():
+    """Two single-read calls with their own workspaces on two streams: each grid wants every
+    compute unit, so some blocks start only when the other call's blocks leave, and their
+    row's resident blocks wait or compute the missing pairs themselves. The bits equal those of
+    one call at a time."""
+    require_gpu()
+    rng = np.random.Generator(np.random.PCG64(11))
+    xa = dev_f16((rng.standard_normal((64, 393216)) * 2.0).astype(np.float16).view(np.uint16))
+    xb = dev_f16((rng.standard_normal((32, 800000)) * 4.0).astype(np.float16).view(np.uint16))
+    ref_a, ref_b = host_bits16(mp.softmax(xa)), host_bits16(mp.softmax(xb))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ya, yb = torch.empty_like(xa), torch.empty_like(xb)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            mp.softmax(xa, y=ya, stream=sa)
+        with torch.cuda.stream(sb):
+            mp.softmax(xb, y=yb, stream=sb)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits16(ya), ref_a)
+        assert np.array_equal(host_bits16(yb), ref_b)
 
 
 def test_softmax_special_values_and_in_place():
