@@ -435,8 +435,9 @@ def c5_sweep(mp, torch, workloads, copy_gbps, reps=5) -> dict:
 
 def c3_gemms(mp, torch, reps=25, M=8192, N=4096, K=4096) -> dict:
     """C3: one linear layer of 8192 tokens, 4096 -> 4096: forward, dgrad and wgrad with binary16
-    outputs, each over `reps` launches after untimed ones (five rounds of all three first, then three
-    of the kind: the chip's clock settles to the load over a few milliseconds). X, dY ~ N(0,1),
+    outputs, each over `reps` launches after untimed ones (fifteen rounds of all three first, ~9 ms,
+    then three of the kind: the chip's clock settles to the load over several milliseconds, and
+    with five rounds the kind timed first still ran ~10 % slow). X, dY ~ N(0,1),
     W ~ N(0, 1/64^2)."""
     g = torch.Generator(device="cuda").manual_seed(3)
     X = torch.randn(M, K, device="cuda", generator=g).half()
@@ -451,7 +452,7 @@ def c3_gemms(mp, torch, reps=25, M=8192, N=4096, K=4096) -> dict:
     flop = 2.0 * M * N * K
     out = {"workload": f"C3: M={M} tokens, N={N}, K={K}, binary16 in and out, FP32 accumulation",
            "gflop_per_launch": round(flop / 1e9, 2)}
-    for _ in range(5):                   # the GEMMs follow microsecond kernels: bring the chip to this load first
+    for _ in range(15):                  # the GEMMs follow microsecond kernels: bring the chip to this load first
         for f in calls.values():
             f()
     for k, f in calls.items():
