@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
                "update": (990844.1, 1972212.6), "nesterov": (990309.5, 1973116.0),
                "adagrad": (993440.6, 1969707.7)},
     "reduce": {"src": ["mp_reduce.hip", "mp_internal.h"],
-               "sha256": "69ec0b052d136f3490060638de4139aa19a0f9f1fe448362d02abdd84602ddb7",
+               "sha256": "74f269033b0c26646b709488d17df8dfdeab6bfc58a65bac8a25f4ae12bbfcb7",
                "bn_stats": (25340.3, 2021.7), "bn_apply": (25140.9, 50176.0), "softmax": (50773.2, 99331.0)},
     "stats": {"src": ["mp_stats.hip", "mp_internal.h"],
               "sha256": "c1702f46e8f4692c3e5763ecf2e69aae3a2535bdecd36abd1217e95bfdd28f18",

@@ -383,9 +383,11 @@ size_t mp_softmax_workspace(int64_t rows, int64_t cols);
  * at most 256 blocks of 204,800 values with the whole grid at most one block
  * per compute unit, x is read once (each block keeps its segment on chip and
  * exchanges its (max, sum) through the workspace); otherwise a two-pass form
- * reads x twice. The result does not depend on timing, but the forms cut rows
- * differently, so their outputs may differ in the last bit. Calls that share a
- * workspace must not overlap.
+ * reads x twice; so does a call made while the stream is being captured into
+ * a graph (the single-read form's per-call tag would repeat on every replay).
+ * The result does not depend on timing, but the forms cut rows differently,
+ * so their outputs may differ in the last bit. Calls that share a workspace
+ * must not overlap.
  * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, rows > 2^31 - 1, ldx or ldy
  * < cols, a null pointer or too small a workspace when rows * cols > 0),
  * MP_ERR_HIP. */

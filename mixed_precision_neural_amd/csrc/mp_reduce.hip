@@ -868,7 +868,17 @@ extern "C" mp_status mp_softmax(const uint16_t* x, int64_t rows, int64_t cols, i
     if (rows > 0x7FFFFFFF) return MP_ERR_INVALID_ARGUMENT;
     hipStream_t s = mp::as_stream(stream);
     const int vec = (mp::aligned16(x) && mp::aligned16(y) && ldx % 8 == 0 && ldy % 8 == 0) ? 8 : 1;
-    if (vec == 8 && static_cast<const void*>(x) != static_cast<const void*>(y)) {
+    // The single-read form's per-call tag is a kernel argument: under stream
+    // capture every replay of the graph would reuse it, and a block could take
+    // the slots of an earlier replay for this one's. A captured call takes the
+    // two-pass form, which keeps nothing between calls.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusActive;
+    if (hipStreamIsCapturing(s, &capture) != hipSuccess) {
+        (void)hipGetLastError();                         // not a launch error of this call
+        capture = hipStreamCaptureStatusActive;
+    }
+    if (vec == 8 && static_cast<const void*>(x) != static_cast<const void*>(y) &&
+        capture == hipStreamCaptureStatusNone) {
         ResPlan p;
         mp_status st = res_plan(rows, cols, workspace_bytes, &p);
         if (st != MP_OK) return st;

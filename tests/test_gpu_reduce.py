@@ -221,6 +221,33 @@ def test_softmax_concurrent_calls_on_two_streams():
         assert np.array_equal(host_bits16(yb), ref_b)
 
 
+def test_softmax_captured_in_a_graph_and_replayed_on_new_inputs():
+    """A call captured into a HIP graph takes the two-pass form (the single-read form's per-call
+    tag would repeat on every replay, and a block could take an earlier replay's slots for this
+    one's). Replayed on three different inputs written into the captured buffer, each replay is
+    within one ulp of the oracle and equal to the two-pass form run eagerly (in place on a copy)."""
+    require_gpu()
+    rows, cols, ld = 64, 393216, 393216
+    rng = np.random.Generator(np.random.PCG64(5))
+    xd = dev_f16((rng.standard_normal((rows, cols)) * 3.0).astype(np.float16).view(np.uint16))
+    yd = torch.empty_like(xd)
+    mp.softmax(xd, y=yd)                       # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mp.softmax(xd, y=yd)                   # recorded, not run
+    for t in range(3):
+        x = (rng.standard_normal((rows, cols)) * (2.0 + t)).astype(np.float16).view(np.uint16)
+        xd.copy_(dev_f16(x))
+        g.replay()
+        torch.cuda.synchronize()
+        got = host_bits16(yd)
+        assert within_ulp(got, oracle.softmax(x)), t
+        two_pass = dev_f16(x)
+        mp.softmax(two_pass, y=two_pass)       # in place: the two-pass form
+        assert np.array_equal(got, host_bits16(two_pass)), t
+
+
 def test_softmax_special_values_and_in_place():
     require_gpu()
     ninf, pinf, nan = 0xFC00, 0x7C00, 0x7E00
