@@ -496,9 +496,9 @@ __global__ __launch_bounds__(kThreads) void softmax_norm_kernel(const uint16_t* 
 // per SIMD, 256 registers each); thread t holds vectors i * 512 + t of its
 // segment in registers, all loads issued before the first use. (Holding part
 // of the segment in LDS instead, loaded straight from memory, was slower: at
-// one block per compute unit that path delivered a third of what register
-// loads did.) Each block computes its
-// segment's (max, sum) in the same per-thread order as the two-pass form's
+// one block per compute unit that path delivered its share well after the
+// register loads had delivered theirs.) Each block computes its segment's
+// (max, sum) with the two-pass form's per-thread online update and block
 // merge, publishes it in a workspace slot tagged with the call's 64-bit tag
 // (release), and its first wave polls the row's other slots (relaxed loads,
 // then one acquire fence). A slot that has not been published within the wait
@@ -540,8 +540,9 @@ struct ResSeg {
 };
 
 // (max, sum) of segment p of the row computed from memory, in the per-thread
-// order of the block that owns it: vectors i * 1024 + t for i = 0, 1, ...,
-// then the row's tail values (last segment only).
+// order of the block that owns it: vectors i * 512 + t for i = 0, 1, ...,
+// nvt - 1 (-inf values past the segment, as the owner loads them), then the
+// row's tail values (last segment only).
 __device__ MaxSum res_pair_from_memory(const uint16_t* xr, int p, int parts, int64_t seg_vecs, int64_t nvec,
                                        int64_t cols, int nvt) {
     const ResSeg sg(p, seg_vecs, nvec);
