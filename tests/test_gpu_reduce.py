@@ -157,6 +157,9 @@ SOFTMAX_SHAPES = [
     (1, 40000005, 40000008),     # single read, 256 blocks, LDS in use, every lane polls 4 slots
     (256, 204795, 204800),       # single read at capacity: one block per row, 25 vectors per thread
     (257, 1000, 1000),           # one row too many for one block per compute unit: two-pass
+    (5, 7, 8),                   # single read, rows shorter than one 16-byte vector: the tail only
+    (3, 8, 8),                   # single read, one vector per row and no tail
+    (200, 300000, 300000),       # one block per row allowed, but a row exceeds 204,800 values: two-pass
 ]
 
 
