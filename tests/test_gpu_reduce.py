@@ -153,9 +153,9 @@ SOFTMAX_SHAPES = [
     (3, 3 * 8192 + 5, 3 * 8192 + 8),   # single read, one block per row, ragged tail
     (2, 50000, 50001),           # element-wise two-pass form, several segments
     (64, 793471, 793472),        # the page's vocabulary: single read, 4 blocks of 24,796 vectors per row
-    (5, 1200003, 1200008),       # single read, 37 blocks per row, registers only
-    (1, 40000005, 40000008),     # single read, 256 blocks, LDS in use, every lane polls 4 slots
-    (256, 204795, 204800),       # single read at capacity: one block per row, 25 vectors per thread
+    (5, 1200003, 1200008),       # single read, 37 blocks per row of 4,055 vectors (8 per thread)
+    (1, 40000005, 40000008),     # single read, 256 blocks of 19,532 vectors: a polling lane watches 4 slots
+    (256, 204795, 204800),       # single read at capacity: one block per row, 50 vectors per thread
     (257, 1000, 1000),           # one row too many for one block per compute unit: two-pass
     (5, 7, 8),                   # single read, rows shorter than one 16-byte vector: the tail only
     (3, 8, 8),                   # single read, one vector per row and no tail
