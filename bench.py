@@ -764,6 +764,21 @@ def main():
     gc.enable()
     ms = start.elapsed_time(end) / args.steps
 
+    # Median and minimum step: the same number of steps once more, each between its own pair
+    # of HIP events (two queue markers per step of ~4.7 ms).
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        a.record()
+        model.step()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in pairs)
+    step_stats = {"median_ms": round(per_step[len(per_step) // 2], 4), "min_ms": round(per_step[0], 4),
+                  "max_ms": round(per_step[-1], 4), "steps": len(per_step),
+                  "method": "one pair of HIP events around each of the same number of further steps"}
+
     # Per-launch durations: the same number of steps once more, each launch between two HIP
     # events on the stream it runs on. They are kept out of the timed steps because every
     # recorded event is a queue marker of its own (~0.25 ms per step for the 76 of a step).
@@ -870,6 +885,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
