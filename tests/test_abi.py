@@ -151,3 +151,23 @@ def test_probe_library_exports_and_validation():
     assert L.mp_probe_mfma_clock(1, 10, probe.RANDOM, k16, None, C.byref(khz), None) == INVALID
     assert L.mp_probe_mfma_clock(1, 10, 2, k16, P, C.byref(khz), None) == INVALID     # unknown operand kind
     assert L.mp_probe_mfma_clock(1, 10, probe.RANDOM, 2, P, C.byref(khz), None) == INVALID   # unknown MFMA form
+
+
+def test_softmax_workspace_and_wait_setting():
+    """The softmax workspace covers either form: the two-pass form's (max, sum) per (row, 32K
+    segment) or the single-read form's 16-byte slot per block (at most 1024 blocks). The
+    single-read wait is a process-wide setting in microseconds: 200 by default, clamped to
+    100000, queried by a negative value, and every call returns the previous setting."""
+    L = mp.lib()
+    assert L.mp_softmax_workspace(0, 5) == 0 and L.mp_softmax_workspace(5, 0) == 0
+    assert L.mp_softmax_workspace(1, 8) == 256 * 16                  # one row: 256 slots
+    assert L.mp_softmax_workspace(64, 793471) == 1024 * 16           # slots capped at 1024 blocks
+    assert L.mp_softmax_workspace(100000, 2 ** 20) == 100000 * 32 * 8  # two-pass pairs dominate
+    prev = L.mp_softmax_wait_us(-1)
+    try:
+        assert prev == 200
+        assert L.mp_softmax_wait_us(0) == 200 and L.mp_softmax_wait_us(-5) == 0
+        assert L.mp_softmax_wait_us(10 ** 9) == 0 and L.mp_softmax_wait_us(-1) == 100000
+    finally:
+        L.mp_softmax_wait_us(prev)
+    assert L.mp_softmax_wait_us(-1) == prev
