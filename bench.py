@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
                "update": (990844.1, 1972212.6), "nesterov": (990309.5, 1973116.0),
                "adagrad": (993440.6, 1969707.7)},
     "reduce": {"src": ["mp_reduce.hip", "mp_internal.h"],
-               "sha256": "66722e41b906f61bf57c89c763ae2caa4a3caf4163f2d1b0064abbfb2d36a5bc",
+               "sha256": "927982e6c2b0543266071f7f09c592a2d1ab6a0943a71527ff97353e27d36193",
                "bn_stats": (25340.3, 2021.7), "bn_apply": (25140.9, 50176.0), "softmax": (50773.2, 99331.0)},
     "stats": {"src": ["mp_stats.hip", "mp_internal.h"],
               "sha256": "c1702f46e8f4692c3e5763ecf2e69aae3a2535bdecd36abd1217e95bfdd28f18",

@@ -352,7 +352,8 @@ size_t mp_bn_stats_workspace(int64_t rows, int64_t channels);
  * `workspace` is caller-owned device memory of at least
  * mp_bn_stats_workspace(rows, channels) bytes, 4-byte aligned, overwritten.
  * Errors: MP_ERR_INVALID_ARGUMENT (rows < 1, channels < 0, ldx < channels, a
- * null pointer or too small a workspace when channels > 0), MP_ERR_HIP. */
+ * null pointer or too small or misaligned a workspace when channels > 0),
+ * MP_ERR_HIP. */
 mp_status mp_bn_stats(const uint16_t* x, int64_t rows, int64_t channels, int64_t ldx, float* mean,
                       float* var, void* workspace, size_t workspace_bytes, mp_stream stream);
 
@@ -389,8 +390,8 @@ size_t mp_softmax_workspace(int64_t rows, int64_t cols);
  * so their outputs may differ in the last bit. Calls that share a workspace
  * must not overlap.
  * Errors: MP_ERR_INVALID_ARGUMENT (negative sizes, rows > 2^31 - 1, ldx or ldy
- * < cols, a null pointer or too small a workspace when rows * cols > 0),
- * MP_ERR_HIP. */
+ * < cols, a null pointer or too small or misaligned a workspace when
+ * rows * cols > 0), MP_ERR_HIP. */
 mp_status mp_softmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
                      void* workspace, size_t workspace_bytes, mp_stream stream);
 

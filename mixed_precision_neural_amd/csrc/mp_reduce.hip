@@ -811,6 +811,7 @@ extern "C" mp_status mp_bn_stats(const uint16_t* x, int64_t rows, int64_t channe
     if (channels == 0) return MP_OK;
     if (!x || !mean || !var || !workspace || workspace_bytes < mp_bn_stats_workspace(rows, channels))
         return MP_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3) != 0) return MP_ERR_INVALID_ARGUMENT;   // FP32 moments
     hipStream_t s = mp::as_stream(stream);
     const int vec = bn_vec(x, ldx, channels);
     const int64_t per = bn_rows_per_chunk(rows, channels, vec);
@@ -866,6 +867,7 @@ extern "C" mp_status mp_softmax(const uint16_t* x, int64_t rows, int64_t cols, i
     if (rows < 0 || cols < 0 || ldx < cols || ldy < cols) return MP_ERR_INVALID_ARGUMENT;
     if (rows == 0 || cols == 0) return MP_OK;
     if (!x || !y || !workspace || workspace_bytes < mp_softmax_workspace(rows, cols)) return MP_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7) != 0) return MP_ERR_INVALID_ARGUMENT;   // 64-bit slots
     if (rows > 0x7FFFFFFF) return MP_ERR_INVALID_ARGUMENT;
     hipStream_t s = mp::as_stream(stream);
     const int vec = (mp::aligned16(x) && mp::aligned16(y) && ldx % 8 == 0 && ldy % 8 == 0) ? 8 : 1;

@@ -155,7 +155,8 @@ def test_probe_library_exports_and_validation():
 
 def test_softmax_workspace_and_wait_setting():
     """The softmax workspace covers either form: the two-pass form's (max, sum) per (row, 32K
-    segment) or the single-read form's 16-byte slot per block (at most 1024 blocks). The
+    segment) or the single-read form's 16-byte slot per block (at most 1024 blocks); a short,
+    misaligned or mis-pitched call is rejected before any launch. The
     single-read wait is a process-wide setting in microseconds: 200 by default, clamped to
     100000, queried by a negative value, and every call returns the previous setting."""
     L = mp.lib()
@@ -163,6 +164,12 @@ def test_softmax_workspace_and_wait_setting():
     assert L.mp_softmax_workspace(1, 8) == 256 * 16                  # one row: 256 slots
     assert L.mp_softmax_workspace(64, 793471) == 1024 * 16           # slots capped at 1024 blocks
     assert L.mp_softmax_workspace(100000, 2 ** 20) == 100000 * 32 * 8  # two-pass pairs dominate
+    nbn = L.mp_bn_stats_workspace(4, 16)
+    assert L.mp_bn_stats(P, 4, 16, 16, P, P, C.c_void_p(0x1002), nbn, None) == INVALID   # misaligned
+    need = L.mp_softmax_workspace(4, 16)
+    assert L.mp_softmax(P, 4, 16, 16, P, 16, C.c_void_p(0x1004), need, None) == INVALID   # misaligned
+    assert L.mp_softmax(P, 4, 16, 16, P, 16, P, need - 8, None) == INVALID               # short
+    assert L.mp_softmax(P, 4, 16, 8, P, 16, P, need, None) == INVALID                    # ldx < cols
     prev = L.mp_softmax_wait_us(-1)
     try:
         assert prev == 200
