@@ -46,18 +46,18 @@ CHECK_BYTES_PER_PARAM = 2
 # source it was taken on: it is reported while the SHA-256 of those files still matches.
 MEASURED_TRAFFIC = {
     "gemm": {"src": ["mp_gemm.hip", "mp_internal.h", "mp_act.h"],
-             "sha256": "fd383788529f6268fc46db7304f2c46c9a36f7a02f20665c9ad84432f8a1b8eb",
+             "sha256": "88fe50202f528eabafbfc0f38ef0fc6ba93db2c600812408147a641ac145ac78",
              "fwd": (98408.8, 32768.0), "fwd_act": (98481.7, 65536.0), "fwd_act_deriv": (98481.7, 65536.0),
              "dgrad_act": (114881.7, 32768.0), "dgrad_mul": (114808.5, 32768.0), "wgrad": (99453.4, 34816.0)},
     "update": {"src": ["mp_step.hip", "mp_internal.h"],
-               "sha256": "e5ea3aff9795752032a623271d7738611019a843dd1fa5fd24887479ee853aeb",
+               "sha256": "675c7fca4abd374d5d1b1b91fee77a9c901bae463135c0c340572a03a10262f0",
                "update": (990844.1, 1972212.6), "nesterov": (990309.5, 1973116.0),
                "adagrad": (993440.6, 1969707.7)},
     "reduce": {"src": ["mp_reduce.hip", "mp_internal.h"],
-               "sha256": "927982e6c2b0543266071f7f09c592a2d1ab6a0943a71527ff97353e27d36193",
+               "sha256": "7109d62b3a4136e5de1a2c9267a43d3256f6dc012907ce095ee3a597a257069b",
                "bn_stats": (25340.3, 2021.7), "bn_apply": (25140.9, 50176.0), "softmax": (50773.2, 99331.0)},
     "stats": {"src": ["mp_stats.hip", "mp_internal.h"],
-              "sha256": "c1702f46e8f4692c3e5763ecf2e69aae3a2535bdecd36abd1217e95bfdd28f18",
+              "sha256": "4857ba544bf243d20e031caef561c1a496e998549740a7590313207240144019",
               "absmax": (394786.6, 7.5)},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0

@@ -33,6 +33,11 @@
  *     are updated in place by design.
  *   - Calls on different streams are safe when their buffers are disjoint;
  *     one mp_scaler belongs to one stream at a time.
+ *   - Device words the kernels update atomically or read whole (an
+ *     mp_scaler, wgrad's found_inf, the |g| maximum and its non-finite flag,
+ *     a loss value) must be 4-byte aligned, and workspaces aligned as each
+ *     call states; a misaligned one is MP_ERR_INVALID_ARGUMENT. Data buffers
+ *     may be unaligned (such calls take an element-wise path).
  */
 #ifndef MP_H
 #define MP_H

@@ -266,7 +266,7 @@ extern "C" mp_status mp_loss_softmax_ce(const uint16_t* logits, const int32_t* l
                                         uint16_t* dlogits, void* workspace, size_t workspace_bytes,
                                         mp_stream stream) {
     if (B < 0 || C < 0) return MP_ERR_INVALID_ARGUMENT;
-    if (!scaler || !loss) return MP_ERR_INVALID_ARGUMENT;
+    if (!scaler || !loss || mp::misaligned4(scaler) || mp::misaligned4(loss)) return MP_ERR_INVALID_ARGUMENT;
     if (B > 0 && C > 0 && (!logits || !labels || !dlogits)) return MP_ERR_INVALID_ARGUMENT;
     if (B == 0 || C == 0) return MP_OK;
     const uint32_t grid = ce_grid(B);
@@ -299,6 +299,7 @@ mp_status loss_mse_into(const uint16_t* y, const uint16_t* t, int64_t M, int64_t
 mp_status loss_mse_args(const uint16_t* y, const uint16_t* t, int64_t M, int64_t N,
                         const mp_scaler* scaler, const float* loss, const uint16_t* dy) {
     if (M < 0 || N < 0 || !scaler || !loss) return MP_ERR_INVALID_ARGUMENT;
+    if (mp::misaligned4(scaler) || mp::misaligned4(loss)) return MP_ERR_INVALID_ARGUMENT;
     if (M > 0 && N > 0 && (!y || !t || !dy)) return MP_ERR_INVALID_ARGUMENT;
     return MP_OK;
 }

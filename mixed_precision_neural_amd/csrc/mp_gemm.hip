@@ -803,6 +803,7 @@ extern "C" mp_status mp_linear_wgrad(const uint16_t* dY, int64_t lddy, const uin
     if (M < 0 || N < 0 || K < 0) return MP_ERR_INVALID_ARGUMENT;
     if (dw_dtype != MP_F16 && dw_dtype != MP_F32) return MP_ERR_INVALID_ARGUMENT;
     if (dw_dtype == MP_F32 && found_inf) return MP_ERR_INVALID_ARGUMENT;
+    if (found_inf && mp::misaligned4(found_inf)) return MP_ERR_INVALID_ARGUMENT;
     if (N == 0 || K == 0) return MP_OK;
     if (bad_matrix(dY, M, N, lddy) || bad_matrix(X, M, K, ldx) || bad_matrix(dW, N, K, lddw))
         return MP_ERR_INVALID_ARGUMENT;

@@ -70,5 +70,7 @@ __device__ __forceinline__ uint32_t nonfinite1(uint16_t h) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// A device word the kernels update atomically or read as a whole (flags, scaler, maxima).
+inline bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
 
 }  // namespace mp

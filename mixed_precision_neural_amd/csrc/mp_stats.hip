@@ -234,7 +234,8 @@ extern "C" mp_status mp_tensor_list_destroy(mp_tensor_list* L) {
 
 extern "C" mp_status mp_absmax(const mp_tensor_list* L, float* amax, uint32_t* nonfinite,
                                mp_stream stream) {
-    if (!L || !amax) return MP_ERR_INVALID_ARGUMENT;
+    if (!L || !amax || mp::misaligned4(amax) || (nonfinite && mp::misaligned4(nonfinite)))
+        return MP_ERR_INVALID_ARGUMENT;
     if (L->chunks == 0) return MP_OK;
     hipStream_t s = mp::as_stream(stream);
     uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
@@ -249,7 +250,8 @@ extern "C" mp_status mp_absmax(const mp_tensor_list* L, float* amax, uint32_t* n
 extern "C" mp_status mp_scaler_init_from_absmax(mp_scaler* scaler, const float* amax, float headroom,
                                                 int32_t dynamic, int32_t growth_interval,
                                                 mp_stream stream) {
-    if (!scaler || !amax || !is_pow2_in_range(headroom)) return MP_ERR_INVALID_ARGUMENT;
+    if (!scaler || !amax || mp::misaligned4(scaler) || mp::misaligned4(amax) || !is_pow2_in_range(headroom))
+        return MP_ERR_INVALID_ARGUMENT;
     if (dynamic && growth_interval < 1) return MP_ERR_INVALID_ARGUMENT;
     scaler_from_absmax_kernel<<<1, 1, 0, mp::as_stream(stream)>>>(scaler, amax, headroom, dynamic ? 1u : 0u,
                                                                   growth_interval);

@@ -372,14 +372,14 @@ mp_status run_step(const mp_param_list* L, int kind, const Hyper& hp, mp_scaler*
 
 extern "C" mp_status mp_step(const mp_param_list* L, mp_sgd hyper, mp_scaler* scaler,
                              uint32_t flags, mp_stream stream) {
-    if (!L || !scaler) return MP_ERR_INVALID_ARGUMENT;
+    if (!L || !scaler || mp::misaligned4(scaler)) return MP_ERR_INVALID_ARGUMENT;
     const Hyper hp{hyper.lr, hyper.momentum, hyper.weight_decay, 0.0f};
     return run_step(L, MP_OPT_SGD, hp, scaler, flags, stream);
 }
 
 extern "C" mp_status mp_step_opt(const mp_param_list* L, mp_optim hyper, mp_scaler* scaler,
                                  uint32_t flags, mp_stream stream) {
-    if (!L || !scaler) return MP_ERR_INVALID_ARGUMENT;
+    if (!L || !scaler || mp::misaligned4(scaler)) return MP_ERR_INVALID_ARGUMENT;
     if (hyper.kind != MP_OPT_SGD && hyper.kind != MP_OPT_NESTEROV && hyper.kind != MP_OPT_ADAGRAD)
         return MP_ERR_INVALID_ARGUMENT;
     if (hyper.kind == MP_OPT_ADAGRAD && !(hyper.eps > 0.0f && hyper.eps <= 3.4028235e38f))
@@ -390,7 +390,7 @@ extern "C" mp_status mp_step_opt(const mp_param_list* L, mp_optim hyper, mp_scal
 
 extern "C" mp_status mp_scaler_init(mp_scaler* scaler, float init_scale, int32_t dynamic,
                                     int32_t growth_interval, mp_stream stream) {
-    if (!scaler || !is_pow2_scale(init_scale)) return MP_ERR_INVALID_ARGUMENT;
+    if (!scaler || mp::misaligned4(scaler) || !is_pow2_scale(init_scale)) return MP_ERR_INVALID_ARGUMENT;
     if (dynamic && growth_interval < 1) return MP_ERR_INVALID_ARGUMENT;
     scaler_init_kernel<<<1, 1, 0, mp::as_stream(stream)>>>(scaler, init_scale, dynamic ? 1u : 0u,
                                                            growth_interval);
@@ -398,7 +398,7 @@ extern "C" mp_status mp_scaler_init(mp_scaler* scaler, float init_scale, int32_t
 }
 
 extern "C" mp_status mp_scaler_update(mp_scaler* scaler, mp_stream stream) {
-    if (!scaler) return MP_ERR_INVALID_ARGUMENT;
+    if (!scaler || mp::misaligned4(scaler)) return MP_ERR_INVALID_ARGUMENT;
     scaler_update_kernel<<<1, 1, 0, mp::as_stream(stream)>>>(scaler);
     return mp::launch_status("mp_scaler_update");
 }

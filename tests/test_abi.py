@@ -178,3 +178,22 @@ def test_softmax_workspace_and_wait_setting():
     finally:
         L.mp_softmax_wait_us(prev)
     assert L.mp_softmax_wait_us(-1) == prev
+
+
+def test_atomic_targets_must_be_word_aligned():
+    """Words the kernels update atomically or read whole (the wgrad overflow flag, the scaler,
+    the running |g| maximum and its non-finite flag, the loss) must be 4-byte aligned; a
+    misaligned one is an argument error before any launch."""
+    L = mp.lib()
+    odd = C.c_void_p(0x1002)
+    assert L.mp_linear_wgrad(P, 64, P, 64, P, 64, 0, 64, 64, 64, odd, None) == INVALID
+    assert L.mp_scaler_init(odd, C.c_float(1024.0), 1, 2000, None) == INVALID
+    assert L.mp_scaler_update(odd, None) == INVALID
+    assert L.mp_loss_mse(P, P, 8, 8, C.c_float(1.0), odd, P, P, P, 1 << 12, None) == INVALID
+    assert L.mp_loss_mse(P, P, 8, 8, C.c_float(1.0), P, odd, P, P, 1 << 12, None) == INVALID
+    assert L.mp_loss_softmax_ce(P, P, 8, 10, odd, P, P, P, 1 << 12, None) == INVALID
+    assert L.mp_scaler_init_from_absmax(odd, P, C.c_float(2.0), 1, 2000, None) == INVALID
+    assert L.mp_scaler_init_from_absmax(P, odd, C.c_float(2.0), 1, 2000, None) == INVALID
+    # the list handles below are never dereferenced: the pointer checks come first
+    assert L.mp_absmax(P, odd, None, None) == INVALID
+    assert L.mp_absmax(P, P, odd, None) == INVALID
